@@ -1,0 +1,266 @@
+"""CPU oracle for the W8A8 scaled-quantized Linear -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``int8_w8a8_quantized_amd``) never imports it, and it imports nothing from
+the product: the two share no code.
+
+The arithmetic lives in ``tfq_oracle.c`` (plain C, binary32 quantisation with
+strict IEEE semantics, exact binary64 GEMM sums); this module only compiles it
+with gcc and marshals numpy arrays through ctypes.  Every function cites the
+page passage it follows in the C source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tfq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libtfq_oracle.so")
+
+QTYPE_E4M3FN = 0
+QTYPE_INT8 = 1
+
+_CFLAGS = [
+    "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+    "-fexcess-precision=standard", "-fopenmp", "-shared", "-fPIC",
+]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libtfq_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.tfq_oracle_bf16_to_f32.restype = ctypes.c_float
+        L.tfq_oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.tfq_oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.tfq_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.tfq_oracle_e4m3fn_value.restype = ctypes.c_double
+        L.tfq_oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
+        L.tfq_oracle_e4m3fn_encode.restype = ctypes.c_uint8
+        L.tfq_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+        L.tfq_oracle_e4m3fn_encode_search.restype = ctypes.c_uint8
+        L.tfq_oracle_e4m3fn_encode_search.argtypes = [ctypes.c_float]
+        L.tfq_oracle_e4m3fn_encode_array.restype = None
+        L.tfq_oracle_e4m3fn_encode_array.argtypes = [P, P, i64]
+        L.tfq_oracle_encoder_mismatches.restype = i64
+        L.tfq_oracle_encoder_mismatches.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P]
+        L.tfq_oracle_quantize_rows.restype = None
+        L.tfq_oracle_quantize_rows.argtypes = [P, i64, i64, i64, ctypes.c_int, ctypes.c_float, i64, P, P]
+        L.tfq_oracle_quantize_blocks.restype = None
+        L.tfq_oracle_quantize_blocks.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_float, i64, P, P]
+        L.tfq_oracle_gelu_tanh.restype = ctypes.c_double
+        L.tfq_oracle_gelu_tanh.argtypes = [ctypes.c_double]
+        L.tfq_oracle_dot.restype = None
+        L.tfq_oracle_dot.argtypes = [P, P, ctypes.c_int, i64, i64, i64, P, i64, P]
+        L.tfq_oracle_linear_ref.restype = None
+        L.tfq_oracle_linear_ref.argtypes = [P, P, P, P, ctypes.c_int, i64, i64, i64, i64, P,
+                                            ctypes.c_int, P, i64, P]
+        L.tfq_oracle_int8_linear.restype = None
+        L.tfq_oracle_int8_linear.argtypes = [P, P, P, P, i64, i64, i64, P, P, i64, P, P]
+        L.tfq_oracle_error_measures.restype = None
+        L.tfq_oracle_error_measures.argtypes = [P, P, i64, P, P]
+        L.tfq_oracle_num_threads.restype = ctypes.c_int
+        L.tfq_oracle_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _qtype(q) -> int:
+    if q in ("fp8", "e4m3fn", QTYPE_E4M3FN):
+        return QTYPE_E4M3FN
+    if q in ("int8", QTYPE_INT8):
+        return QTYPE_INT8
+    raise ValueError(f"unknown qtype {q!r}")
+
+
+def num_threads() -> int:
+    return lib().tfq_oracle_num_threads()
+
+
+# --------------------------------------------------------------------------
+# scalar helpers
+# --------------------------------------------------------------------------
+def bf16_to_f32(h: int) -> float:
+    return lib().tfq_oracle_bf16_to_f32(h)
+
+
+def f32_to_bf16(v: float) -> int:
+    return lib().tfq_oracle_f32_to_bf16(v)
+
+
+def e4m3fn_value(code: int) -> float:
+    """Closed-form E4M3FN decode of one code (OCP OFP8)."""
+    return lib().tfq_oracle_e4m3fn_value(code)
+
+
+def e4m3fn_encode(v: float) -> int:
+    """E4M3FN encoder 1 (field arithmetic, RNE, saturating)."""
+    return lib().tfq_oracle_e4m3fn_encode(v)
+
+
+def e4m3fn_encode_search(v: float) -> int:
+    """E4M3FN encoder 2 (nearest-value search, ties to even code)."""
+    return lib().tfq_oracle_e4m3fn_encode_search(v)
+
+
+def e4m3fn_encode_array(v: np.ndarray) -> np.ndarray:
+    """Encoder 1 applied elementwise to a float32 array."""
+    a = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib().tfq_oracle_e4m3fn_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def encoder_mismatches(first_bits: int, last_bits: int) -> tuple[int, int]:
+    """Count binary32 patterns in [first, last] (both signs) where the two
+    encoders disagree; returns (count, first bad pattern or 0xFFFFFFFF)."""
+    fb = ctypes.c_uint32(0)
+    n = lib().tfq_oracle_encoder_mismatches(first_bits, last_bits, ctypes.byref(fb))
+    return int(n), int(fb.value)
+
+
+def gelu_tanh(h: float) -> float:
+    return lib().tfq_oracle_gelu_tanh(h)
+
+
+def e4m3fn_table() -> np.ndarray:
+    """Values of all 256 codes (NaN for 0x7F and 0xFF)."""
+    return np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# array functions
+# --------------------------------------------------------------------------
+def quantize_rows(x_bf16: np.ndarray, qtype, qmax: float, group: int = 0):
+    """Per-row (group=0) or per-1xgroup dynamic absmax quantisation.
+
+    x_bf16: uint16 [rows, cols] (BF16 bits). Returns (codes uint8 [rows, cols],
+    scales float32 [rows] or [rows, ceil(cols/group)])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    ng = 1 if group <= 0 else (cols + group - 1) // group
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((rows, ng), dtype=np.float32)
+    lib().tfq_oracle_quantize_rows(_ptr(x), rows, cols, cols, _qtype(qtype), float(qmax),
+                                   int(group), _ptr(q), _ptr(s))
+    return q, (s[:, 0].copy() if group <= 0 else s)
+
+
+def quantize_blocks(w_bf16: np.ndarray, qtype, qmax: float, block: int = 128):
+    """One scale per block x block tile of W [n, k]."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    n, k = w.shape
+    nb, kb = (n + block - 1) // block, (k + block - 1) // block
+    q = np.empty((n, k), dtype=np.uint8)
+    s = np.empty((nb, kb), dtype=np.float32)
+    lib().tfq_oracle_quantize_blocks(_ptr(w), n, k, _qtype(qtype), float(qmax), int(block),
+                                     _ptr(q), _ptr(s))
+    return q, s
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.shape[0])
+
+
+def dot(a_q: np.ndarray, b_q: np.ndarray, qtype, rows=None) -> np.ndarray:
+    """Exact sum_k a[m,k] b[n,k] of decoded codes, binary64, for selected rows."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    b = np.ascontiguousarray(b_q).view(np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    out = np.empty((R, N), dtype=np.float64)
+    lib().tfq_oracle_dot(_ptr(a), _ptr(b), _qtype(qtype), M, N, K, _ptr(r), nr, _ptr(out))
+    return out
+
+
+def linear_ref(a_q, a_scale, b_q, b_scale, qtype, scale_block: int = 0, bias=None,
+               gelu: bool = False, rows=None) -> np.ndarray:
+    """Scaled Linear reference y [R, N] in binary64 (see tfq_oracle_linear_ref)."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    b = np.ascontiguousarray(b_q).view(np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    sa = np.ascontiguousarray(a_scale, dtype=np.float32)
+    sb = np.ascontiguousarray(b_scale, dtype=np.float32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    out = np.empty((R, N), dtype=np.float64)
+    lib().tfq_oracle_linear_ref(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _qtype(qtype), M, N, K,
+                                int(scale_block), _ptr(bi), 1 if gelu else 0, _ptr(r), nr,
+                                _ptr(out))
+    return out
+
+
+def int8_linear(a_q, a_scale, b_q, b_scale, bias=None, rows=None, want_acc=True,
+                want_bf16=True):
+    """INT8 W8A8: (acc int64 [R,N] or None, y bf16 bits uint16 [R,N] or None)."""
+    a = np.ascontiguousarray(a_q).view(np.int8)
+    b = np.ascontiguousarray(b_q).view(np.int8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    sa = np.ascontiguousarray(a_scale, dtype=np.float32)
+    sb = np.ascontiguousarray(b_scale, dtype=np.float32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    acc = np.empty((R, N), dtype=np.int64) if want_acc else None
+    y = np.empty((R, N), dtype=np.uint16) if want_bf16 else None
+    lib().tfq_oracle_int8_linear(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(bi),
+                                 _ptr(r), nr, _ptr(acc), _ptr(y))
+    return acc, y
+
+
+def error_measures(yq: np.ndarray, y: np.ndarray) -> tuple[float, float]:
+    """(E_max, E_rel) of the pages' operator comparison."""
+    a = np.ascontiguousarray(yq, dtype=np.float64).ravel()
+    b = np.ascontiguousarray(y, dtype=np.float64).ravel()
+    emax = ctypes.c_double(0)
+    erel = ctypes.c_double(0)
+    lib().tfq_oracle_error_measures(_ptr(a), _ptr(b), a.shape[0], ctypes.byref(emax),
+                                    ctypes.byref(erel))
+    return emax.value, erel.value
+
+
+def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    """Exact decode of BF16 bit arrays (upper half of binary32)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
