@@ -1,0 +1,323 @@
+"""Benchmark of the W8A8 scaled-quantized Linear on one MI355X.
+
+A step is one pass of the hot path over the video-DiT FFN pair (X [75600,
+5120] BF16, W_up [13824, 5120], W_down [5120, 13824], activation qmax 448):
+
+    quantise X per token -> FP8 GEMM with GELU-tanh epilogue -> G [75600, 13824]
+    -> quantise G per token -> FP8 GEMM -> Y [75600, 5120]
+
+with the weights quantised per output channel once, before timing (they are
+cached on first use).  Inputs are seeded synthetic data already resident in
+HBM.  The JSON line reports whole-step TFLOP/s (4 M N K flops per step), the
+roofline of the dominant kernel (the up-projection GEMM, timed with HIP events
+on the stream it runs on), the oracle timed on host cores on a row sample,
+and per-workload extras (image-DiT FFN-up fused Linear, block-scaled FP8,
+INT8, quantiser GB/s).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class EventTimer:
+    """Per-kernel durations from HIP events recorded on the launch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.pairs: dict[str, list] = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record(self.stream)
+        out = fn()
+        e.record(self.stream)
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def ms(self, name) -> list[float]:
+        return [s.elapsed_time(e) for s, e in self.pairs.get(name, [])]
+
+    def clear(self):
+        self.pairs.clear()
+
+
+def quant_bytes(m, k, group=0):
+    return 3 * m * k + 4 * m * (k // group if group else 1)
+
+
+def time_calls(torch, stream, fn, reps=20, warmup=5):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    t = sorted(s.elapsed_time(e) for s, e in evs)
+    return t[len(t) // 2], t[0]
+
+
+def extras(torch, tfq, synth, stream):
+    """Secondary workloads, each timed on its own (median of 20 after 5 warmup)."""
+    out = {}
+    # image-DiT FFN-up: one fused call (quantise X + GEMM)
+    log("extras: c3_image_dit")
+    d = synth.make("c3_image_dit")
+    M, K, N = d["spec"].M, d["spec"].K, d["spec"].N
+    x, w = dev_bf16(d["x"], torch), dev_bf16(d["w"], torch)
+    del d
+    wq, ws = tfq.tfq_quantize_weight_per_channel(w, "fp8", 448.0)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    need = tfq.tfq_quant_linear_workspace_bytes(M, K, "fp8", 0)
+    wsp = torch.empty(need, dtype=torch.uint8, device="cuda")
+    med, best = time_calls(torch, stream, lambda: tfq.tfq_quant_linear_fused(
+        x, wq, ws, "fp8", 448.0, 0, None, None, y, wsp))
+    fl = 2.0 * M * N * K
+    out["c3_image_dit_fused_linear"] = {"ms": med, "ms_min": best, "tflops": fl / med / 1e9,
+                                        "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS}
+    qa, sa = tfq.tfq_quantize_rows(x, "fp8", 448.0)
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 0, qa, sa))
+    gbs = quant_bytes(M, K) / med / 1e6
+    out["c3_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 0, None,
+                                                                      None, y))
+    out["c3_gemm"] = {"ms": med, "tflops": fl / med / 1e9,
+                      "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS}
+    del x, w, wq, ws, y, wsp, qa, sa
+
+    # block-scaled FP8
+    log("extras: c5_block_fp8")
+    d = synth.make("c5_block_fp8")
+    M, K, N = d["spec"].M, d["spec"].K, d["spec"].N
+    x, w = dev_bf16(d["x"], torch), dev_bf16(d["w"], torch)
+    del d
+    wq, ws = tfq.tfq_quantize_weight_per_channel(w, "fp8", 448.0, 128)
+    qa, sa = tfq.tfq_quantize_rows(x, "fp8", 448.0, 128)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 128, qa, sa))
+    gbs = quant_bytes(M, K, 128) / med / 1e6
+    out["c5_quantize_x_groups"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    fl = 2.0 * M * N * K
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 128, None,
+                                                                      None, y))
+    out["c5_block_gemm"] = {"ms": med, "tflops": fl / med / 1e9,
+                            "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS}
+    del x, w, wq, ws, y, qa, sa
+
+    # INT8
+    log("extras: c2_int8")
+    d = synth.make("c2_int8")
+    M, K, N = d["spec"].M, d["spec"].K, d["spec"].N
+    x, w = dev_bf16(d["x"], torch), dev_bf16(d["w"], torch)
+    del d
+    wq, ws = tfq.tfq_quantize_weight_per_channel(w, "int8", 127.0)
+    qa, sa = tfq.tfq_quantize_rows(x, "int8", 127.0)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "int8", 127.0, 0, qa, sa))
+    gbs = quant_bytes(M, K) / med / 1e6
+    out["c2_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    fl = 2.0 * M * N * K
+    med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_int8(qa, sa, wq, ws, None, None,
+                                                                       True, False, y))
+    out["c2_int8_gemm"] = {"ms": med, "tops": fl / med / 1e9,
+                           "frac_int8_peak": fl / med / 1e9 / INT8_PEAK_TOPS}
+    return out
+
+
+def cpu_baseline(d, rows_sample: int):
+    """The oracle on host cores over a row sample of the same FFN-pair step:
+    quantise the sampled X rows, up GEMM + GELU, BF16 round, quantise G rows,
+    down GEMM.  Returns (TFLOP/s, seconds, threads)."""
+    import oracle as orc
+    import synth
+
+    x = np.ascontiguousarray(d["x"][:rows_sample])
+    wq_up, ws_up = orc.quantize_rows(d["w"], "fp8", 448.0)
+    wq_dn, ws_dn = orc.quantize_rows(d["w_down"], "fp8", 448.0)
+    t0 = time.perf_counter()
+    qx, sx = orc.quantize_rows(x, "fp8", 448.0)
+    g = orc.linear_ref(qx, sx, wq_up, ws_up, "fp8", gelu=True)
+    gb = synth.to_bf16_bits(g.astype(np.float32))
+    qg, sg = orc.quantize_rows(gb, "fp8", 448.0)
+    orc.linear_ref(qg, sg, wq_dn, ws_dn, "fp8")
+    sec = time.perf_counter() - t0
+    M, N = rows_sample, d["w"].shape[0]
+    K = d["w"].shape[1]
+    flops = 4.0 * M * N * K
+    return flops / sec / 1e12, sec, orc.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--qmax", type=float, default=448.0)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int8_w8a8_quantized_amd as tfq
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    log("generating c4_video_dit inputs (seeded synthetic)")
+    t0 = time.perf_counter()
+    d = synth.make("c4_video_dit")
+    spec = d["spec"]
+    M, K, N, N2 = spec.M, spec.K, spec.N, spec.n_down
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s: X [{M},{K}] W_up [{N},{K}] "
+        f"W_down [{N2},{N}]")
+    x = dev_bf16(d["x"], torch)
+    w_up = dev_bf16(d["w"], torch)
+    w_dn = dev_bf16(d["w_down"], torch)
+    # one-time weight quantisation (cached on first use), outside the timed region
+    wq_up, ws_up = tfq.tfq_quantize_weight_per_channel(w_up, "fp8", 448.0)
+    wq_dn, ws_dn = tfq.tfq_quantize_weight_per_channel(w_dn, "fp8", 448.0)
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+    g = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    qg = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    sg = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    timer = EventTimer(torch, stream)
+
+    def step(qmax):
+        timer.run("quant_x", lambda: tfq.tfq_quantize_rows(x, "fp8", qmax, 0, qx, sx))
+        timer.run("gemm_up_gelu", lambda: tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None,
+                                                                 "gelu_tanh", g))
+        timer.run("quant_g", lambda: tfq.tfq_quantize_rows(g, "fp8", qmax, 0, qg, sg))
+        timer.run("gemm_down", lambda: tfq.tfq_scaled_mm_fp8(qg, sg, wq_dn, ws_dn, 0, None, None,
+                                                              y))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(args.qmax)
+    torch.cuda.synchronize()
+    timer.clear()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(args.qmax)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    flops_step = 4.0 * M * N * K
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    per = {k: float(np.mean(timer.ms(k))) for k in ("quant_x", "gemm_up_gelu", "quant_g",
+                                                       "gemm_down")}
+    up_flops = 2.0 * M * N * K
+    achieved = up_flops / (per["gemm_up_gelu"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "scaled_gemm fp8 (up projection + GELU epilogue)",
+                "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    kernels = {
+        "quant_x": {"ms": per["quant_x"], "gbs": quant_bytes(M, K) / per["quant_x"] / 1e6},
+        "gemm_up_gelu": {"ms": per["gemm_up_gelu"], "tflops": achieved},
+        "quant_g": {"ms": per["quant_g"], "gbs": quant_bytes(M, N) / per["quant_g"] / 1e6},
+        "gemm_down": {"ms": per["gemm_down"],
+                      "tflops": 2.0 * M * N2 * N / (per["gemm_down"] * 1e-3) / 1e12},
+    }
+    for kk in ("quant_x", "quant_g"):
+        kernels[kk]["frac_hbm"] = kernels[kk]["gbs"] / HBM_PEAK_GBS
+    log(f"step {ms_step:.3f} ms -> {value:.1f} TFLOP/s; per kernel {json.dumps(per)}")
+
+    # the reduced-qmax sweep: same work, one timed step each
+    sweep = {}
+    for q in (14.0, 7.0):
+        step(q)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            step(q)
+        torch.cuda.synchronize()
+        sweep[str(q)] = {"ms_per_step": (time.perf_counter() - t1) * 1e3 / 3}
+    timer.clear()
+
+    ext = {}
+    if not args.no_extras:
+        del x, g, qg, y, qx
+        torch.cuda.empty_cache()
+        ext = extras(torch, tfq, synth, stream)
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows of the same step")
+        tf, sec, thr = cpu_baseline(d, args.cpu_rows)
+        cpu = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
+               "sample": f"{args.cpu_rows} of {M} token rows of the FFN-pair step (quantise X, "
+                         f"up GEMM + GELU, quantise G, down GEMM), {sec:.1f} s"}
+
+    out = {
+        "metric": "FP8 W8A8 Linear TFLOP/s (% FP8 MFMA peak) + quantize GB/s at DiT shapes",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn (fp32 accumulate)",
+        "data": "synthetic (seeded; Student-t(4) activations, N(0,0.015) weights)",
+        "config": {"workload": "video-DiT FFN pair: X[75600,5120] -> W_up[13824,5120] + "
+                               "GELU-tanh -> W_down[5120,13824], per-token/per-channel E4M3FN",
+                   "M": M, "K": K, "N_up": N, "N_down": N2, "act_qmax": args.qmax,
+                   "frac_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "qmax_sweep": sweep,
+        "extras": ext,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

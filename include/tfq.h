@@ -1,0 +1,209 @@
+/*
+ * tfq.h -- C ABI of the MI355X (gfx950) W8A8 scaled-quantized Linear.
+ *
+ * The method (web pages, cited by title and section):
+ *   - TeleFuser "Quantization", "Core ideas": symmetric INT8,
+ *     s = max|x| / 127, q = clamp(round(x / s), -128, 127), x_hat = s q; one
+ *     scale may cover a tensor, an output channel, a token or a block.
+ *   - TeleFuser "Quantization", "Scaled FP8 checkpoints: W8A8": every input
+ *     row quantised to E4M3FN with s = max|x| / max(E4M3FN),
+ *     q = cast_E4M3FN(clamp(x / s)); then a scaled GEMM back to BF16.
+ *   - TeleFuser "Quantization", "tf-kernel FP8: online W8A8": activations
+ *     quantised per token at each forward, weights per output channel and
+ *     cached on first use, BF16 output; single GPU.
+ *   - LightX2V "模型量化技术", "MiniMax-H3 FP8 FP16 累加": row-dynamic
+ *     activation scale = max(abs(x)) / qmax with reduced qmax (14, 12, 7);
+ *     table "量化模式", fp8-b128-deepgemm: block-symmetric FP8 weights and
+ *     group-symmetric FP8 activations.
+ *   - vLLM-Omni "FP8 Quantization", "Parameters": weight_block_size.
+ *
+ * Arithmetic contract (readings of what the pages leave open):
+ *   s = RN32(amax / qmax); t = RN32(x / s) (correctly rounded division);
+ *   FP8: code = E4M3FN_RNE(clamp(t, -qmax, qmax)), sign of zero kept;
+ *   INT8: code = clamp(round_half_even(t), -128, 127);
+ *   an all-zero row/group stores s = 0 and signed-zero codes;
+ *   GEMM: y[m,n] = s_a[m] * s_b[n] * sum_k a[m,k] b[n,k] accumulated in
+ *   FP32 (FP8) or exactly in INT32 (INT8), rounded once to BF16 (RNE);
+ *   INT8 BF16 output is bf16(RN(RN(float(acc) * s_a[m]) * s_b[n]) [+ bias]);
+ *   block mode: y = sum_kb s_a[m,kb] s_b[n/128,kb] (sum_{k in kb} a b).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates or frees memory and keeps no pointer after a
+ *     call returns.  Matrices are row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; no call synchronises the host.
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check returns a status and enqueues nothing.  Nothing throws or aborts
+ *     across the ABI.  Calls are thread-safe (per-device state is set up
+ *     once under a lock).
+ *   - The current HIP device must be a gfx950; otherwise
+ *     TFQ_ERR_UNSUPPORTED_DEVICE.  There is no fallback path.
+ *   - Inputs must be finite (behaviour for NaN/Inf inputs is unspecified).
+ */
+#ifndef TFQ_H
+#define TFQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TFQ_ABI_VERSION 1
+
+typedef enum tfq_status {
+    TFQ_OK = 0,
+    TFQ_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+    TFQ_ERR_BAD_SHAPE = 2,          /* a size is out of range or not a multiple it must be */
+    TFQ_ERR_MISALIGNED = 3,         /* a pointer or leading dimension breaks 16-byte alignment */
+    TFQ_ERR_BAD_QMAX = 4,           /* qmax not finite, <= 0, too large, or not on the code grid */
+    TFQ_ERR_WORKSPACE_TOO_SMALL = 5,/* fused Linear workspace smaller than required */
+    TFQ_ERR_ALIAS = 6,              /* an output overlaps an input or another output */
+    TFQ_ERR_UNSUPPORTED = 7,        /* an enum value or option combination that is not provided */
+    TFQ_ERR_UNSUPPORTED_DEVICE = 8, /* no HIP device, or the current device is not gfx950 */
+    TFQ_ERR_HIP = 9                 /* a HIP runtime call failed; see tfq_last_hip_error() */
+} tfq_status;
+
+typedef enum tfq_qtype {
+    TFQ_QTYPE_E4M3FN = 0,  /* OCP FP8 E4M3FN codes (uint8), qmax on the E4M3FN grid, <= 448 */
+    TFQ_QTYPE_INT8 = 1     /* symmetric INT8 codes (int8), integer qmax in [1, 127] */
+} tfq_qtype;
+
+typedef enum tfq_epilogue {
+    TFQ_EPI_NONE = 0,      /* y = scaled product (+ bias) */
+    TFQ_EPI_GELU_TANH = 1  /* y = gelu_tanh(scaled product (+ bias)), computed in FP32 */
+} tfq_epilogue;
+
+/*
+ * Per-token (row-wise) dynamic absmax quantisation of BF16 activations.
+ * TeleFuser "Quantization", "Scaled FP8 checkpoints: W8A8" (FP8 rows) and
+ * "Core ideas" (INT8); LightX2V "模型量化技术", "MiniMax-H3 FP8 FP16 累加"
+ * (reduced qmax); group_cols = 128 is the 1x128 token-group scaling of
+ * fp8-b128-deepgemm (LightX2V, table "量化模式").
+ *
+ *   x_bf16    [rows, cols] BF16, row stride ld_x elements (ld_x >= cols,
+ *             ld_x % 8 == 0), 16-byte aligned.
+ *   qtype     TFQ_QTYPE_E4M3FN or TFQ_QTYPE_INT8; qmax as in tfq_qtype.
+ *   group_cols 0 = one scale per row; 128 = one scale per 1x128 group
+ *             (cols % 128 == 0).
+ *   q_out     [rows, cols] codes, dense (row stride cols), 16-byte aligned.
+ *   scale_out [rows] FP32, or [rows, cols/128] for group_cols = 128.
+ *   rows >= 1; cols >= 16, cols % 16 == 0.
+ */
+tfq_status tfq_quantize_rows(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                             int32_t qtype, float qmax, int32_t group_cols, void* q_out,
+                             float* scale_out, void* stream);
+
+/*
+ * Weight quantisation, one absmax scale per output channel (row of W) or per
+ * 128x128 block.  TeleFuser "Quantization", "Offline conversion" (one absmax
+ * scale per output row for int8 and fp8) and "tf-kernel FP8: online W8A8"
+ * (weights quantised per output channel, cached by the caller on first use);
+ * LightX2V table "量化模式" (fp8-b128-deepgemm block-symmetric weights) and
+ * vLLM-Omni "Parameters" (weight_block_size).
+ *
+ *   w_bf16    [n, k] BF16, dense, 16-byte aligned.
+ *   block     0 = per output channel (scale_out [n]);
+ *             128 = per 128x128 block (scale_out [n/128, k/128]; n % 128 == 0
+ *             and k % 128 == 0).
+ *   q_out     [n, k] codes, 16-byte aligned.
+ *   n >= 1; k >= 16, k % 16 == 0.
+ */
+tfq_status tfq_quantize_weight_per_channel(const void* w_bf16, int64_t n, int64_t k, int32_t qtype,
+                                           float qmax, int32_t block, void* q_out,
+                                           float* scale_out, void* stream);
+
+/*
+ * Scaled FP8 (E4M3FN x E4M3FN, FP32 accumulation) GEMM with the scale
+ * epilogue fused into the BF16 store: y = a . b^T scaled per row and column.
+ * TeleFuser "Quantization", "tf-kernel FP8: online W8A8" (fp8_scaled_mm
+ * produces BF16) and "Scaled FP8 checkpoints: W8A8"; block mode follows
+ * LightX2V table "量化模式" (fp8-b128-deepgemm).
+ *
+ *   a_q [m, k] codes (activations), b_q [n, k] codes (weights, one output
+ *   channel per row): both K-contiguous, 16-byte aligned.
+ *   scale_block 0:   a_scale [m], b_scale [n].
+ *   scale_block 128: a_scale [m, k/128] (1x128 groups), b_scale [n/128, k/128]
+ *                    (128x128 blocks); k % 128 == 0, n % 128 == 0.
+ *   bias_bf16  [n] BF16 or NULL, added after scaling (before GELU).
+ *   epi        tfq_epilogue.
+ *   y_bf16     [m, n] BF16, 16-byte aligned.
+ *   m >= 1; n >= 8, n % 8 == 0; k >= 16, k % 16 == 0.
+ */
+tfq_status tfq_scaled_mm_fp8(const uint8_t* a_q, const float* a_scale, const uint8_t* b_q,
+                             const float* b_scale, int64_t m, int64_t n, int64_t k,
+                             int32_t scale_block, const void* bias_bf16, int32_t epi, void* y_bf16,
+                             void* stream);
+
+/*
+ * Scaled INT8 GEMM (INT32 accumulation, exact): symmetric INT8 of TeleFuser
+ * "Quantization", "Core ideas", per-token activations and per-channel
+ * weights.
+ *
+ *   a_q [m, k], b_q [n, k] int8 codes, 16-byte aligned; a_scale [m],
+ *   b_scale [n]; bias_bf16 [n] or NULL; epi tfq_epilogue.
+ *   y_bf16  [m, n] BF16 output or NULL.
+ *   acc_i32 [m, n] raw INT32 accumulators or NULL (16-byte aligned).
+ *   At least one of y_bf16 / acc_i32 must be given.
+ *   m >= 1; n >= 8, n % 8 == 0; 16 <= k <= 131071, k % 16 == 0 (so no INT32
+ *   sum can overflow: 131071 * 128 * 128 < 2^31).
+ */
+tfq_status tfq_scaled_mm_int8(const int8_t* a_q, const float* a_scale, const int8_t* b_q,
+                              const float* b_scale, int64_t m, int64_t n, int64_t k,
+                              const void* bias_bf16, int32_t epi, void* y_bf16, int32_t* acc_i32,
+                              void* stream);
+
+/*
+ * Bytes of workspace tfq_quant_linear_fused needs: the activation codes
+ * [m, k] followed (at a 256-byte boundary) by the activation scales.
+ * Returns 0 for invalid arguments.
+ */
+size_t tfq_quant_linear_workspace_bytes(int64_t m, int64_t k, int32_t qtype, int32_t scale_block);
+
+/*
+ * The W8A8 Linear forward: quantise the BF16 activations per token (or per
+ * 1x128 group when scale_block = 128) into the workspace, then run the scaled
+ * GEMM against already-quantised weights, on one stream.  TeleFuser
+ * "Quantization", "tf-kernel FP8: online W8A8" and "Scaled FP8 checkpoints:
+ * W8A8" (LinearFP8: quantise each input row every forward, scaled GEMM, BF16
+ * out).
+ *
+ *   x_bf16 [m, k] (row stride ld_x) BF16 activations; w_q [n, k] codes and
+ *   w_scale ([n], or [n/128, k/128] for scale_block 128) from
+ *   tfq_quantize_weight_per_channel; qtype applies to both operands;
+ *   act_qmax the activation qmax; bias_bf16 [n] or NULL; epi tfq_epilogue;
+ *   block mode (scale_block = 128) is FP8 only;
+ *   y_bf16 [m, n]; workspace of at least
+ *   tfq_quant_linear_workspace_bytes(m, k, qtype, scale_block) bytes,
+ *   256-byte aligned, owned by the caller and not used concurrently by
+ *   another call.
+ */
+tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                  const void* w_q, const float* w_scale, int64_t n, int32_t qtype,
+                                  float act_qmax, int32_t scale_block, const void* bias_bf16,
+                                  int32_t epi, void* y_bf16, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * The device's own E4M3FN encoder (round-to-nearest-even, saturating to
+ * +-448, sign of zero kept) applied to n FP32 values: the cast of TeleFuser
+ * "Quantization", "Scaled FP8 checkpoints: W8A8", exposed on its own so that
+ * the conversion the quantiser uses can be checked over all binary32 inputs.
+ *   x [n] FP32, q [n] codes, both 16-byte aligned; n >= 1, n % 4 == 0.
+ */
+tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* tfq_status_string(tfq_status s);
+/* hipError_t of the last TFQ_ERR_HIP returned on the calling thread (0 if none). */
+int tfq_last_hip_error(void);
+/* TFQ_ABI_VERSION of the library. */
+int tfq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TFQ_H */

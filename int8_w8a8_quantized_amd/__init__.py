@@ -1,0 +1,190 @@
+"""MI355X (gfx950) W8A8 scaled-quantized Linear.
+
+Thin Python binding over the C ABI of ``include/tfq.h`` (``libtfq.so``): every
+function below has the name of the C entry point it calls and only marshals
+arguments -- torch tensors supply device memory and the current HIP stream;
+all quantisation and GEMM work runs in the library's HIP kernels.  There is
+no CPU or PyTorch fallback: a missing library or a failing call raises.
+
+Method (web pages, cited by title and section): TeleFuser "Quantization",
+"tf-kernel FP8: online W8A8" (per-token activation quantisation at each
+forward, per-output-channel weights quantised and cached on first use, BF16
+output) and "Core ideas" (symmetric INT8); LightX2V "模型量化技术", table
+"量化模式" (fp8-b128-deepgemm block scaling) and "MiniMax-H3 FP8 FP16 累加"
+(reduced activation qmax).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import TfqError, check, lib
+
+__all__ = [
+    "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
+    "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
+    "tfq_quant_linear_fused", "tfq_e4m3fn_encode_f32", "tfq_abi_version", "QuantLinear",
+]
+
+QTYPE = {"fp8": 0, "e4m3fn": 0, "int8": 1}
+EPI = {None: 0, "none": 0, "gelu_tanh": 1, "gelu": 1}
+
+
+def _qt(qtype) -> int:
+    return QTYPE[qtype] if isinstance(qtype, str) else int(qtype)
+
+
+def _epi(epi) -> int:
+    return EPI[epi] if (epi is None or isinstance(epi, str)) else int(epi)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _code_dtype(qt: int):
+    return torch.uint8 if qt == 0 else torch.int8
+
+
+def tfq_abi_version() -> int:
+    return lib().tfq_abi_version()
+
+
+def tfq_quantize_rows(x: torch.Tensor, qtype="fp8", qmax: float = 448.0, group_cols: int = 0,
+                      q_out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                      stream=None):
+    """Per-token absmax quantisation of BF16 rows x [rows, cols] (row stride
+    x.stride(0)).  Returns (codes [rows, cols], scales [rows] or
+    [rows, cols/128])."""
+    qt = _qt(qtype)
+    rows, cols = x.shape
+    if q_out is None:
+        q_out = torch.empty((rows, cols), dtype=_code_dtype(qt), device=x.device)
+    if scale_out is None:
+        shape = (rows,) if group_cols == 0 else (rows, cols // max(group_cols, 1))
+        scale_out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    check(lib().tfq_quantize_rows(_ptr(x), rows, cols, x.stride(0), qt, float(qmax),
+                                  int(group_cols), _ptr(q_out), _ptr(scale_out), _stream(stream)),
+          "tfq_quantize_rows")
+    return q_out, scale_out
+
+
+def tfq_quantize_weight_per_channel(w: torch.Tensor, qtype="fp8", qmax: float = 448.0,
+                                    block: int = 0, q_out=None, scale_out=None, stream=None):
+    """Weights W [n, k] BF16 -> (codes [n, k], scales [n] or [n/128, k/128])."""
+    qt = _qt(qtype)
+    n, k = w.shape
+    if q_out is None:
+        q_out = torch.empty((n, k), dtype=_code_dtype(qt), device=w.device)
+    if scale_out is None:
+        shape = (n,) if block == 0 else (n // block, k // block)
+        scale_out = torch.empty(shape, dtype=torch.float32, device=w.device)
+    check(lib().tfq_quantize_weight_per_channel(_ptr(w), n, k, qt, float(qmax), int(block),
+                                                _ptr(q_out), _ptr(scale_out), _stream(stream)),
+          "tfq_quantize_weight_per_channel")
+    return q_out, scale_out
+
+
+def tfq_scaled_mm_fp8(a_q, a_scale, b_q, b_scale, scale_block: int = 0, bias=None, epi=None,
+                      y=None, stream=None):
+    """y [m, n] BF16 = (a_q [m,k] . b_q [n,k]^T) scaled per row / column (or per block)."""
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    check(lib().tfq_scaled_mm_fp8(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n, k,
+                                  int(scale_block), _ptr(bias), _epi(epi), _ptr(y),
+                                  _stream(stream)), "tfq_scaled_mm_fp8")
+    return y
+
+
+def tfq_scaled_mm_int8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, want_y: bool = True,
+                       want_acc: bool = False, y=None, acc=None, stream=None):
+    """INT8 scaled GEMM; returns (y BF16 or None, acc INT32 or None)."""
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=a_q.device)
+    check(lib().tfq_scaled_mm_int8(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n, k,
+                                   _ptr(bias), _epi(epi), _ptr(y), _ptr(acc), _stream(stream)),
+          "tfq_scaled_mm_int8")
+    return y, acc
+
+
+def tfq_quant_linear_workspace_bytes(m: int, k: int, qtype="fp8", scale_block: int = 0) -> int:
+    return int(lib().tfq_quant_linear_workspace_bytes(m, k, _qt(qtype), int(scale_block)))
+
+
+def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0,
+                           scale_block: int = 0, bias=None, epi=None, y=None, workspace=None,
+                           stream=None):
+    """The W8A8 Linear forward: quantise x [m, k] per token, then the scaled
+    GEMM against pre-quantised weights; returns y [m, n] BF16."""
+    qt = _qt(qtype)
+    m, k = x.shape
+    n = w_q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    need = tfq_quant_linear_workspace_bytes(m, k, qt, scale_block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check(lib().tfq_quant_linear_fused(_ptr(x), m, k, x.stride(0), _ptr(w_q), _ptr(w_scale), n, qt,
+                                       float(act_qmax), int(scale_block), _ptr(bias), _epi(epi),
+                                       _ptr(y), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)), "tfq_quant_linear_fused")
+    return y
+
+
+def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):
+    """The device's E4M3FN encoder over a float32 tensor (numel % 4 == 0)."""
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    check(lib().tfq_e4m3fn_encode_f32(_ptr(x), _ptr(q), x.numel(), _stream(stream)),
+          "tfq_e4m3fn_encode_f32")
+    return q
+
+
+class QuantLinear:
+    """W8A8 Linear holding a BF16 weight [out, in]: the weight is quantised per
+    output channel (or per 128x128 block) on the first call and kept resident,
+    activations are quantised per token (or per 1x128 group) on every call
+    (TeleFuser "Quantization", "tf-kernel FP8: online W8A8")."""
+
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, qtype="fp8",
+                 act_qmax: float | None = None, weight_qmax: float | None = None,
+                 scale_block: int = 0, epi=None):
+        self.weight = weight
+        self.bias = bias
+        self.qtype = qtype
+        default = 448.0 if _qt(qtype) == 0 else 127.0
+        self.act_qmax = default if act_qmax is None else act_qmax
+        self.weight_qmax = default if weight_qmax is None else weight_qmax
+        self.scale_block = scale_block
+        self.epi = epi
+        self.w_q = None
+        self.w_scale = None
+        self._ws = None
+
+    def quantized_weight(self):
+        if self.w_q is None:
+            self.w_q, self.w_scale = tfq_quantize_weight_per_channel(
+                self.weight, self.qtype, self.weight_qmax, self.scale_block)
+        return self.w_q, self.w_scale
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+        w_q, w_s = self.quantized_weight()
+        need = tfq_quant_linear_workspace_bytes(x.shape[0], x.shape[1], self.qtype,
+                                                self.scale_block)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        return tfq_quant_linear_fused(x, w_q, w_s, self.qtype, self.act_qmax, self.scale_block,
+                                      self.bias, self.epi, y, self._ws)

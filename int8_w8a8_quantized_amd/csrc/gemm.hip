@@ -1,0 +1,330 @@
+// Scaled W8A8 GEMM for gfx950 (CDNA4): y = (a . b^T) * s_a[m] * s_b[n] -> BF16.
+//
+// Method: TeleFuser "Quantization", "tf-kernel FP8: online W8A8" (per-token
+// FP8 activations x per-output-channel FP8 weights -> BF16 via a scaled
+// GEMM) and "Core ideas" (symmetric INT8, x_hat = s q, so the product of the
+// dequantised operands factors into s_a s_b (q_a . q_b)); block mode follows
+// LightX2V "模型量化技术", table "量化模式" (fp8-b128-deepgemm): one scale per
+// 1x128 activation group and per 128x128 weight block, applied per K-block.
+//
+// Design (MI355X):
+//  * both operands are K-contiguous ("TN"), the layout the MFMA operands want;
+//  * 256x256 output tile per workgroup, 4 waves in a 2x2 grid, 128x128 per
+//    wave = 8x8 v_mfma_f32_16x16x128_f8f6f4 (FP8) or 2x 8x8
+//    v_mfma_i32_16x16x64_i8 (INT8) per 128-deep K step; accumulators live in
+//    the AGPR half of the 512-entry register file (one wave per SIMD);
+//  * global -> LDS through 128-bit buffer loads (out-of-range rows and the K
+//    tail read as zero, so ragged M/N/K need no extra branches), staged in
+//    registers while the MFMAs of the current K step run, double-buffered
+//    LDS (2 x 64 KB of the 160 KB), one barrier per K step;
+//  * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
+//    the row's low 3 bits so that the MFMA fragment reads (16 rows x 16 B per
+//    8 lanes) hit distinct banks;
+//  * the K order inside an MFMA is irrelevant to the sum as long as A and B
+//    use the same one, so each lane group simply reads 32 contiguous bytes;
+//  * tile order: consecutive workgroup ids go round-robin over the 8 XCDs,
+//    so ids are remapped to give each XCD a contiguous slice of the tile
+//    sequence, and the sequence walks bands of 8 tile rows so that the 32
+//    tiles in flight on one XCD share A and B panels in that XCD's L2;
+//  * epilogue: FP32 (acc * s_a) * s_b [+ bias] [GELU-tanh] -> BF16 (RNE); the
+//    INT8 path converts the exact INT32 sum to FP32 first and rounds each
+//    product in a fixed order (bit-reproducible); raw INT32 output is optional.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "tfq_internal.h"
+
+namespace tfq {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int A_BYTES = BM * BK;                 // 32 KB
+constexpr int B_BYTES = BN * BK;                 // 32 KB
+constexpr int SA_BYTES = BM * 4;                 // block-mode activation scales of one K step
+constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+constexpr int GROUP_M = 8;
+
+struct Params {
+    const uint8_t* a;
+    const uint8_t* b;
+    const float* sa;
+    const float* sb;
+    const uint16_t* bias;
+    uint16_t* y;
+    int32_t* acc;
+    int m, n, k;
+    int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int total = tiles_m * tiles_n;
+    const int full = total & ~7;
+    int id = bid;
+    if (bid < full) id = (bid & 7) * (full >> 3) + (bid >> 3);
+    const int band_tiles = GROUP_M * tiles_n;
+    const int band = id / band_tiles;
+    const int first = band * GROUP_M;
+    const int gm = min(tiles_m - first, GROUP_M);
+    const int in = id - band * band_tiles;
+    tm = first + in % gm;
+    tn = in / gm;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    // v_cvt_pk_bf16_f32: round-to-nearest-even
+    return __builtin_bit_cast(uint16_t, __float2bfloat16(f));
+}
+
+// (v * s_row) * s_col and + bias, each rounded on its own (never fused into
+// an FMA): the fixed order that makes the INT8 BF16 output reproducible.
+__device__ __forceinline__ float scale_out(float v, float srow, float scol)
+{
+#pragma clang fp contract(off)
+    const float t = v * srow;
+    return t * scol;
+}
+
+__device__ __forceinline__ float add_bias(float v, float b)
+{
+#pragma clang fp contract(off)
+    return v + b;
+}
+
+// GELU, tanh form: 0.5 h (1 + tanh(u)) = h / (1 + exp(-2u)),
+// u = sqrt(2/pi) (h + 0.044715 h^3)
+__device__ __forceinline__ float gelu_tanh(float h)
+{
+    const float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+    const float c2 = c1 * 0.044715f;
+    const float z = h * __builtin_fmaf(c2, h * h, c1);
+    const float e = __builtin_amdgcn_exp2f(z);
+    return h * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int QT, bool BLOCK, int EPI, bool WANT_Y, bool WANT_ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void scaled_gemm_kernel(const Params p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = p.k;
+    const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+
+    // global -> LDS: thread t moves chunk (t & 7) of rows (t >> 3) + 32 j
+    const int cc = t & 7, rr = t >> 3;
+    const int voff = rr * K + cc * 16;
+    const int row_stride32 = 32 * K;
+    const int lds_w = rr * BK + ((cc ^ (rr & 7)) << 4);
+
+    // LDS -> MFMA fragments: lane reads row (lane & 15), bytes [32 g, 32 g + 32)
+    const int fr = lane & 15, g = lane >> 4;
+    const int rd0 = fr * BK + (((2 * g) ^ (lane & 7)) << 4);
+    const int rd1 = fr * BK + (((2 * g + 1) ^ (lane & 7)) << 4);
+    const int a_rd = wm * 128 * BK;
+    const int b_rd = A_BYTES + wn * 128 * BK;
+
+    const int KT = (K + BK - 1) / BK;
+
+    v4u ga[8], gb[8];
+    float gs = 0.0f;  // block mode: this thread's activation scale of the next K step
+    const int kblocks = K >> 7;
+
+    auto gload = [&](int kt) {
+        const int k0 = kt * BK;
+        const bool kin = (k0 + cc * 16) < K;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int off = kin ? voff + j * row_stride32 + k0 : (int)0x80000000;
+            ga[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            gb[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        }
+        if constexpr (BLOCK) gs = (t < rows_a) ? p.sa[(int64_t)(m0 + t) * kblocks + kt] : 0.0f;
+    };
+    auto lstore = [&](int stage) {
+        uint8_t* s = smem + stage * STAGE;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            *reinterpret_cast<v4u*>(s + lds_w + j * 32 * BK) = ga[j];
+            *reinterpret_cast<v4u*>(s + A_BYTES + lds_w + j * 32 * BK) = gb[j];
+        }
+        if constexpr (BLOCK) reinterpret_cast<float*>(s + A_BYTES + B_BYTES)[t] = gs;
+    };
+
+    typedef typename std::conditional<QT == kE4M3FN, v4f, v4i>::type acc_t;
+    acc_t acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) gload(kt + 1);
+        const uint8_t* s = smem + cur * STAGE;
+
+        v8i bf[8];
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+            const v4i lo = *reinterpret_cast<const v4i*>(s + b_rd + ni * 16 * BK + rd0);
+            const v4i hi = *reinterpret_cast<const v4i*>(s + b_rd + ni * 16 * BK + rd1);
+            bf[ni] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        float sbk = 0.0f;
+        if constexpr (BLOCK) {
+            const int nb = (n0 + wn * 128) >> 7;
+            sbk = (n0 + wn * 128 < p.n) ? p.sb[(int64_t)nb * kblocks + kt] : 0.0f;
+        }
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            const v4i lo = *reinterpret_cast<const v4i*>(s + a_rd + mi * 16 * BK + rd0);
+            const v4i hi = *reinterpret_cast<const v4i*>(s + a_rd + mi * 16 * BK + rd1);
+            if constexpr (QT == kE4M3FN) {
+                const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                if constexpr (!BLOCK) {
+#pragma unroll
+                    for (int ni = 0; ni < 8; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            af, bf[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
+                } else {
+                    // this lane's 4 rows of the mi-th 16-row slab
+                    const v4f sr = *reinterpret_cast<const v4f*>(
+                        s + A_BYTES + B_BYTES + (wm * 128 + mi * 16 + 4 * g) * 4);
+                    const v4f f = sr * sbk;
+#pragma unroll
+                    for (int ni = 0; ni < 8; ++ni) {
+                        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            af, bf[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[mi][ni][r] = __builtin_fmaf(part[r], f[r], acc[mi][ni][r]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    const v8i b8 = bf[ni];
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        lo, v4i{b8[0], b8[1], b8[2], b8[3]}, acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        hi, v4i{b8[4], b8[5], b8[6], b8[7]}, acc[mi][ni], 0, 0, 0);
+                }
+            }
+        }
+        if (kt + 1 < KT) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    // MFMA 16x16 output layout: lane holds rows 4*(lane>>4) + r (r = 0..3) of
+    // column (lane & 15) of each 16x16 tile.
+    float scol[8], bcol[8];
+    int col[8];
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+        col[ni] = n0 + wn * 128 + ni * 16 + fr;
+        const bool ok = col[ni] < p.n;
+        if constexpr (!BLOCK) scol[ni] = ok ? p.sb[col[ni]] : 0.0f;
+        bcol[ni] = (p.bias != nullptr && ok) ? bf16_to_f32(p.bias[col[ni]]) : 0.0f;
+    }
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + wm * 128 + mi * 16 + 4 * g + r;
+            if (row >= p.m) continue;
+            float srow = 1.0f;
+            if constexpr (!BLOCK) srow = p.sa[row];
+            uint16_t* yr = WANT_Y ? p.y + (int64_t)row * p.n : nullptr;
+            int32_t* ar = WANT_ACC ? p.acc + (int64_t)row * p.n : nullptr;
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni) {
+                if (col[ni] >= p.n) continue;
+                if constexpr (WANT_ACC) ar[col[ni]] = acc[mi][ni][r];
+                if constexpr (WANT_Y) {
+                    float v;
+                    if constexpr (QT == kE4M3FN) {
+                        if constexpr (BLOCK) v = acc[mi][ni][r];
+                        else v = scale_out(acc[mi][ni][r], srow, scol[ni]);
+                    } else {
+                        v = scale_out((float)acc[mi][ni][r], srow, scol[ni]);
+                    }
+                    if (p.bias != nullptr) v = add_bias(v, bcol[ni]);
+                    if constexpr (EPI == 1) v = gelu_tanh(v);
+                    yr[col[ni]] = f32_to_bf16(v);
+                }
+            }
+        }
+    }
+}
+
+template <int QT, bool BLOCK, int EPI, bool WANT_Y, bool WANT_ACC>
+hipError_t launch_one(const Params& p, hipStream_t st)
+{
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    hipLaunchKernelGGL((scaled_gemm_kernel<QT, BLOCK, EPI, WANT_Y, WANT_ACC>), dim3(grid),
+                       dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
+{
+    Params p;
+    p.a = g.a;
+    p.b = g.b;
+    p.sa = g.sa;
+    p.sb = g.sb;
+    p.bias = g.bias;
+    p.y = g.y;
+    p.acc = g.acc;
+    p.m = (int)g.m;
+    p.n = (int)g.n;
+    p.k = (int)g.k;
+    p.tiles_m = (int)((g.m + BM - 1) / BM);
+    p.tiles_n = (int)((g.n + BN - 1) / BN);
+    if (g.qtype == kE4M3FN) {
+        if (g.scale_block == 128)
+            return g.epi == 1 ? launch_one<kE4M3FN, true, 1, true, false>(p, stream)
+                              : launch_one<kE4M3FN, true, 0, true, false>(p, stream);
+        return g.epi == 1 ? launch_one<kE4M3FN, false, 1, true, false>(p, stream)
+                          : launch_one<kE4M3FN, false, 0, true, false>(p, stream);
+    }
+    const bool y = g.y != nullptr, a = g.acc != nullptr;
+    if (g.epi == 1) {
+        if (y && a) return launch_one<kInt8, false, 1, true, true>(p, stream);
+        if (y) return launch_one<kInt8, false, 1, true, false>(p, stream);
+        return launch_one<kInt8, false, 1, false, true>(p, stream);
+    }
+    if (y && a) return launch_one<kInt8, false, 0, true, true>(p, stream);
+    if (y) return launch_one<kInt8, false, 0, true, false>(p, stream);
+    return launch_one<kInt8, false, 0, false, true>(p, stream);
+}
+
+}  // namespace tfq

@@ -1,0 +1,342 @@
+// Dynamic absmax quantisation kernels for gfx950 (CDNA4, wave64).
+//
+// Method: TeleFuser "Quantization", "Core ideas" (symmetric INT8,
+// s = max|x|/127, q = clamp(round(x/s), -128, 127)) and "Scaled FP8
+// checkpoints: W8A8" (per input row, s = max|x| / max(E4M3FN),
+// q = cast_E4M3FN(clamp(x/s))); LightX2V "模型量化技术", "MiniMax-H3 FP8 FP16
+// 累加" (scale = max(abs(x))/qmax with reduced qmax) and table "量化模式"
+// (fp8-b128-deepgemm: 1x128 activation groups, 128x128 weight blocks).
+//
+// The kernels are HBM-bound (2 bytes in, 1 byte out per element):
+//  * one wavefront per row, the whole row held in VGPRs between the absmax
+//    pass and the encode pass (single HBM read), 128-bit loads, 64-bit code
+//    stores, fully coalesced across the wave;
+//  * the absmax is taken on the BF16 bit patterns with the sign cleared
+//    (non-negative finite floats order like integers) using packed 16-bit
+//    max, then reduced with DPP row operations and four readlanes;
+//  * x / s is evaluated as q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0)
+//    with r = RN(1/s) (Markstein's correction step).  For s >= 2^-90 this
+//    equals the correctly rounded quotient whenever |x/s| >= 2^-12 (checked
+//    exhaustively over every BF16 amax / BF16 x pair for the qmax values the
+//    ABI accepts); smaller quotients encode to zero either way and the sign
+//    is restored from x.  Rows with s < 2^-90 or s > 2^126 (including an
+//    overflowed s = inf, where x / s = +-0) use a true division.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tfq_internal.h"
+
+namespace tfq {
+namespace {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    us2 x = __builtin_bit_cast(us2, a), y = __builtin_bit_cast(us2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+__device__ __forceinline__ uint32_t abs_max_chunk(uint32_t m, const uint4& v)
+{
+    m = pk_max_u16(m, v.x & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.y & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.z & 0x7FFF7FFFu);
+    m = pk_max_u16(m, v.w & 0x7FFF7FFFu);
+    return m;
+}
+
+// max over the 16 lanes of a DPP row; every lane of the row gets the result
+__device__ __forceinline__ uint32_t row16_max(uint32_t m)
+{
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false)); // row_half_mirror
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false)); // row_mirror
+    return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t m)
+{
+    m = row16_max(m);
+    uint32_t a = __builtin_amdgcn_readlane(m, 0), b = __builtin_amdgcn_readlane(m, 16);
+    uint32_t c = __builtin_amdgcn_readlane(m, 32), d = __builtin_amdgcn_readlane(m, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// RN(x / s) for the quantiser; see the file comment.
+struct Quotient {
+    float s, r;
+    bool fast;
+    __device__ __forceinline__ explicit Quotient(float scale)
+    {
+        s = scale;
+        fast = (scale >= 0x1p-90f && scale <= 0x1p126f) || (scale == 0.0f);
+        r = (scale == 0.0f) ? 0.0f : 1.0f / scale;  // correctly rounded reciprocal
+    }
+    __device__ __forceinline__ float operator()(float x) const
+    {
+        float q;
+        if (fast) {
+            float q0 = x * r;
+            float e = __builtin_fmaf(-q0, s, x);
+            q = __builtin_fmaf(e, r, q0);
+        } else {
+            q = x / s;
+        }
+        return __builtin_copysignf(q, x);  // also gives signed zeros for s == 0
+    }
+};
+
+template <int QT>
+__device__ __forceinline__ uint32_t encode4(float t0, float t1, float t2, float t3, float qmax)
+{
+    t0 = __builtin_amdgcn_fmed3f(t0, -qmax, qmax);
+    t1 = __builtin_amdgcn_fmed3f(t1, -qmax, qmax);
+    t2 = __builtin_amdgcn_fmed3f(t2, -qmax, qmax);
+    t3 = __builtin_amdgcn_fmed3f(t3, -qmax, qmax);
+    if constexpr (QT == kE4M3FN) {
+        // gfx950 converts to OCP E4M3FN with round-to-nearest-even
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, v, true);
+        return (uint32_t)v;
+    } else {
+        // |t| <= qmax <= 127 after the clamp: round half to even, then pack
+        uint32_t b0 = (uint32_t)(int)__builtin_rintf(t0) & 0xFFu;
+        uint32_t b1 = (uint32_t)(int)__builtin_rintf(t1) & 0xFFu;
+        uint32_t b2 = (uint32_t)(int)__builtin_rintf(t2) & 0xFFu;
+        uint32_t b3 = (uint32_t)(int)__builtin_rintf(t3) & 0xFFu;
+        return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <int QT>
+__device__ __forceinline__ uint2 encode_chunk(const uint4& v, const Quotient& d, float qmax)
+{
+    uint2 o;
+    o.x = encode4<QT>(d(bf_lo(v.x)), d(bf_hi(v.x)), d(bf_lo(v.y)), d(bf_hi(v.y)), qmax);
+    o.y = encode4<QT>(d(bf_lo(v.z)), d(bf_hi(v.z)), d(bf_lo(v.w)), d(bf_hi(v.w)), qmax);
+    return o;
+}
+
+constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
+
+// Per-row quantisation with the row resident in registers (cols <= CH*512).
+template <int QT, int CH>
+__global__ __launch_bounds__(256) void quantize_rows_resident(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+    uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    const int nchunk = (int)(cols >> 3);
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = c * 64 + lane;
+        v[c] = (idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) m = abs_max_chunk(m, v[c]);
+    m = max(m & 0xFFFFu, m >> 16);
+    const uint32_t mw = wave_max(m);
+    const float amax = __uint_as_float(mw << 16);
+    const float s = amax / qmax;  // correctly rounded (IEEE division)
+    if (lane == 0) scale[row] = s;
+    const Quotient d(s);
+    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = c * 64 + lane;
+        if (idx < nchunk) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
+    }
+}
+
+// Per-row quantisation of long rows: an absmax pass, then a second read.
+template <int QT>
+__global__ __launch_bounds__(256) void quantize_rows_two_pass(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+    uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    const int64_t nchunk = cols >> 3;
+    uint32_t m = 0;
+    for (int64_t idx = lane; idx < nchunk; idx += 64) m = abs_max_chunk(m, xr[idx]);
+    m = max(m & 0xFFFFu, m >> 16);
+    const float amax = __uint_as_float(wave_max(m) << 16);
+    const float s = amax / qmax;
+    if (lane == 0) scale[row] = s;
+    const Quotient d(s);
+    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    for (int64_t idx = lane; idx < nchunk; idx += 64) qr[idx] = encode_chunk<QT>(xr[idx], d, qmax);
+}
+
+// 1x128 groups: 16 lanes x 8 elements cover one group, so every chunk of a
+// wave holds 4 whole groups and no row needs to stay resident.
+template <int QT>
+__global__ __launch_bounds__(256) void quantize_groups128(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+    uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    const int nchunk = (int)(cols >> 3);  // multiple of 16
+    const int ngroups = (int)(cols >> 7);
+    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    float* sr = scale + row * ngroups;
+    constexpr int U = 4;
+    for (int base = 0; base < nchunk; base += 64 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * 64 + lane;
+            v[u] = (idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * 64 + lane;
+            uint32_t m = abs_max_chunk(0u, v[u]);
+            m = max(m & 0xFFFFu, m >> 16);
+            m = row16_max(m);  // the group's absmax in every lane of the group
+            const float s = __uint_as_float(m << 16) / qmax;
+            if (idx < nchunk) {
+                if ((lane & 15) == 0) sr[idx >> 4] = s;
+                const Quotient d(s);
+                qr[idx] = encode_chunk<QT>(v[u], d, qmax);
+            }
+        }
+    }
+}
+
+// 128x128 weight blocks: one workgroup (256 threads) per block.
+template <int QT>
+__global__ __launch_bounds__(256) void quantize_blocks128(
+    const uint16_t* __restrict__ w, int64_t n, int64_t k, float qmax, uint8_t* __restrict__ q,
+    float* __restrict__ scale)
+{
+    __shared__ uint32_t red[4];
+    const int64_t kb_count = k >> 7;
+    const int64_t nb = blockIdx.x / kb_count, kb = blockIdx.x % kb_count;
+    const int t = threadIdx.x;
+    // 128 rows x 16 chunks of 8 elements; thread t takes chunk t%16 of rows t/16 + 16 i
+    const int cc = t & 15, r0 = t >> 4;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = nb * 128 + r0 + 16 * i;
+        v[i] = reinterpret_cast<const uint4*>(w + row * k + kb * 128)[cc];
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = abs_max_chunk(m, v[i]);
+    m = max(m & 0xFFFFu, m >> 16);
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float s = __uint_as_float(m << 16) / qmax;
+    if (t == 0) scale[nb * kb_count + kb] = s;
+    const Quotient d(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = nb * 128 + r0 + 16 * i;
+        reinterpret_cast<uint2*>(q + row * k + kb * 128)[cc] = encode_chunk<QT>(v[i], d, qmax);
+    }
+}
+
+__global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float4* __restrict__ x,
+                                                            uint32_t* __restrict__ q, int64_t n4)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 v = x[i];
+    q[i] = encode4<kE4M3FN>(v.x, v.y, v.z, v.w, 448.0f);
+}
+
+template <int QT, int CH>
+hipError_t launch_resident(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+                           uint8_t* q, float* s, hipStream_t st)
+{
+    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((quantize_rows_resident<QT, CH>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       x, rows, cols, ld, qmax, q, s);
+    return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+                          uint8_t* q, float* s, hipStream_t st)
+{
+    const int64_t chunks = (cols >> 3);
+    const int64_t per_lane = (chunks + 63) / 64;
+    if (per_lane <= 2) return launch_resident<QT, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 4) return launch_resident<QT, 4>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 6) return launch_resident<QT, 6>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 8) return launch_resident<QT, 8>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 10) return launch_resident<QT, 10>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 12) return launch_resident<QT, 12>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 16) return launch_resident<QT, 16>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 20) return launch_resident<QT, 20>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 24) return launch_resident<QT, 24>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 28) return launch_resident<QT, 28>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 32) return launch_resident<QT, 32>(x, rows, cols, ld, qmax, q, s, st);
+    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((quantize_rows_two_pass<QT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       rows, cols, ld, qmax, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                int qtype, float qmax, int group_cols, uint8_t* q, float* scale,
+                                hipStream_t stream)
+{
+    if (group_cols == 128) {
+        const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+        if (qtype == kE4M3FN)
+            hipLaunchKernelGGL((quantize_groups128<kE4M3FN>), dim3((unsigned)blocks), dim3(256), 0,
+                               stream, x, rows, cols, ld, qmax, q, scale);
+        else
+            hipLaunchKernelGGL((quantize_groups128<kInt8>), dim3((unsigned)blocks), dim3(256), 0,
+                               stream, x, rows, cols, ld, qmax, q, scale);
+        return hipGetLastError();
+    }
+    if (qtype == kE4M3FN) return launch_rows_qt<kE4M3FN>(x, rows, cols, ld, qmax, q, scale, stream);
+    return launch_rows_qt<kInt8>(x, rows, cols, ld, qmax, q, scale, stream);
+}
+
+hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int qtype, float qmax,
+                                  uint8_t* q, float* scale, hipStream_t stream)
+{
+    const int64_t blocks = (n >> 7) * (k >> 7);
+    if (qtype == kE4M3FN)
+        hipLaunchKernelGGL((quantize_blocks128<kE4M3FN>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, w, n, k, qmax, q, scale);
+    else
+        hipLaunchKernelGGL((quantize_blocks128<kInt8>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, w, n, k, qmax, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3fn_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream)
+{
+    const int64_t n4 = n >> 2;
+    const int64_t blocks = (n4 + 255) / 256;
+    hipLaunchKernelGGL(e4m3fn_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(q), n4);
+    return hipGetLastError();
+}
+
+}  // namespace tfq

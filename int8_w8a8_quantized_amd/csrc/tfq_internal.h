@@ -1,0 +1,44 @@
+// Internal declarations shared by the host dispatch (abi.cpp) and the HIP
+// kernel launchers.  Not part of the public ABI (include/tfq.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tfq {
+
+enum QType : int { kE4M3FN = 0, kInt8 = 1 };
+
+// Launchers enqueue kernels on `stream` and return the launch status.  They
+// assume the arguments already passed the host-side validation.
+
+// Row-wise (group_cols == 0) or 1x128-group (group_cols == 128) quantisation.
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                int qtype, float qmax, int group_cols, uint8_t* q, float* scale,
+                                hipStream_t stream);
+
+// 128x128 block weight quantisation (n % 128 == 0, k % 128 == 0).
+hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int qtype, float qmax,
+                                  uint8_t* q, float* scale, hipStream_t stream);
+
+// Device E4M3FN encoder over n floats (n % 4 == 0).
+hipError_t launch_e4m3fn_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
+
+struct GemmArgs {
+    const uint8_t* a;      // [m, k] codes
+    const uint8_t* b;      // [n, k] codes
+    const float* sa;       // [m] or [m, k/128]
+    const float* sb;       // [n] or [n/128, k/128]
+    const uint16_t* bias;  // [n] BF16 or null
+    uint16_t* y;           // [m, n] BF16 or null
+    int32_t* acc;          // [m, n] INT32 or null (INT8 only)
+    int64_t m, n, k;
+    int qtype;
+    int scale_block;       // 0 or 128
+    int epi;               // 0 none, 1 gelu-tanh
+};
+
+hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace tfq

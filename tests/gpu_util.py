@@ -1,0 +1,64 @@
+"""Helpers for the GPU parity tests: host <-> device transfers and the FP8
+output tolerance stated for the scaled GEMM."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
+
+
+def say(msg: str) -> None:
+    """Name the case (shape, seed, entry point) before a GPU step, flushed."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    """BF16 bit array (uint16) -> device bfloat16 tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_u8(a: np.ndarray, dtype=torch.uint8) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).cuda()
+    return t if dtype == torch.uint8 else t.view(dtype)
+
+
+def dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy raw bits (uint8 for codes, uint16 for bf16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.uint8, torch.int8):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(
+        np.float32).astype(np.float64)
+
+
+def assert_fp8_tolerance(y_bits: np.ndarray, y_ref: np.ndarray, what: str = "") -> float:
+    """max|y - y_ref| <= 2^-7 |y_ref| + 1e-3 max_row|y_ref|, element by
+    element; returns the largest ratio of error to allowance."""
+    y = bf16_to_f64(y_bits)
+    assert y.shape == y_ref.shape
+    rowmax = np.abs(y_ref).max(axis=1, keepdims=True)
+    allow = 2.0 ** -7 * np.abs(y_ref) + 1e-3 * rowmax
+    err = np.abs(y - y_ref)
+    assert np.all(np.isfinite(y)), what
+    bad = err > allow
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} outputs out of tolerance, first at {tuple(i)}: "
+                             f"y={y[tuple(i)]!r} ref={y_ref[tuple(i)]!r} allow={allow[tuple(i)]!r}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(allow > 0, err / allow, 0.0)
+    return float(ratio.max())

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+* libtfq.so loads and exports every function include/tfq.h declares;
+* every invalid-argument path returns its status before any HIP call
+  (fake, never-dereferenced addresses are passed: these tests are skipped on
+  a machine that has a GPU so that a validation bug can never launch a kernel
+  on them);
+* on a machine without a GPU a valid call reports TFQ_ERR_UNSUPPORTED_DEVICE
+  instead of falling back to anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HAS_GPU_NODE = os.path.exists("/dev/kfd")
+
+OK, NULL, SHAPE, ALIGN, QMAX, WS, ALIAS, UNSUP, DEV, HIP = range(10)
+
+# fake 256-byte-aligned addresses, far apart; never dereferenced
+A, B, C, D, E, F, G = (0x10_0000_0000 * (i + 1) for i in range(7))
+
+no_gpu_only = pytest.mark.skipif(HAS_GPU_NODE, reason="fake-pointer validation tests run only "
+                                 "on machines without a GPU")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from int8_w8a8_quantized_amd._lib import lib
+
+    return lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tfq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tfq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), n
+    from int8_w8a8_quantized_amd._lib import SIGNATURES
+
+    assert sorted(s[0] for s in SIGNATURES) == names
+
+
+def test_version_and_strings(L):
+    assert L.tfq_abi_version() == 1
+    for s in range(10):
+        assert L.tfq_status_string(s)
+    assert L.tfq_last_hip_error() == 0
+
+
+@no_gpu_only
+def test_quantize_rows_validation(L):
+    q = L.tfq_quantize_rows
+    assert q(None, 4, 64, 64, 0, 448.0, 0, B, C, None) == NULL
+    assert q(A, 4, 64, 64, 0, 448.0, 0, None, C, None) == NULL
+    assert q(A, 0, 64, 64, 0, 448.0, 0, B, C, None) == SHAPE
+    assert q(A, 4, 60, 64, 0, 448.0, 0, B, C, None) == SHAPE      # cols % 16
+    assert q(A, 4, 64, 32, 0, 448.0, 0, B, C, None) == SHAPE      # ld < cols
+    assert q(A, 4, 64, 68, 0, 448.0, 0, B, C, None) == ALIGN      # ld % 8
+    assert q(A + 2, 4, 64, 64, 0, 448.0, 0, B, C, None) == ALIGN
+    assert q(A, 4, 64, 64, 0, 448.0, 0, B + 8, C, None) == ALIGN
+    assert q(A, 4, 64, 64, 2, 448.0, 0, B, C, None) == UNSUP      # qtype
+    assert q(A, 4, 64, 64, 0, 448.0, 64, B, C, None) == UNSUP     # group size
+    assert q(A, 4, 192, 192, 0, 448.0, 128, B, C, None) == SHAPE  # cols % 128 in group mode
+    for bad in (0.0, -1.0, 449.0, 21.0, float("inf"), float("nan")):
+        assert q(A, 4, 64, 64, 0, bad, 0, B, C, None) == QMAX, bad
+    assert q(A, 4, 64, 64, 1, 127.5, 0, B, C, None) == QMAX
+    assert q(A, 4, 64, 64, 1, 128.0, 0, B, C, None) == QMAX
+    assert q(A, 4, 64, 64, 0, 448.0, 0, A + 64, C, None) == ALIAS  # codes over x
+    assert q(A, 4, 64, 64, 0, 448.0, 0, B, B + 128, None) == ALIAS  # scales over codes
+
+
+@no_gpu_only
+def test_weight_quantize_validation(L):
+    w = L.tfq_quantize_weight_per_channel
+    assert w(A, 256, 256, 0, 448.0, 64, B, C, None) == UNSUP
+    assert w(A, 200, 256, 0, 448.0, 128, B, C, None) == SHAPE
+    assert w(A, 256, 200, 0, 448.0, 128, B, C, None) == SHAPE
+    assert w(None, 256, 256, 0, 448.0, 128, B, C, None) == NULL
+
+
+@no_gpu_only
+def test_gemm_validation(L):
+    f = L.tfq_scaled_mm_fp8
+    assert f(A, B, C, D, 64, 64, 64, 0, None, 0, None, None) == NULL
+    assert f(None, B, C, D, 64, 64, 64, 0, None, 0, E, None) == NULL
+    assert f(A, B, C, D, 64, 60, 64, 0, None, 0, E, None) == SHAPE   # n % 8
+    assert f(A, B, C, D, 64, 64, 40, 0, None, 0, E, None) == SHAPE   # k % 16
+    assert f(A, B, C, D, 0, 64, 64, 0, None, 0, E, None) == SHAPE
+    assert f(A, B, C, D, 64, 64, 64, 64, None, 0, E, None) == UNSUP  # scale_block
+    assert f(A, B, C, D, 64, 64, 192, 128, None, 0, E, None) == SHAPE
+    assert f(A, B, C, D, 64, 64, 64, 0, None, 5, E, None) == UNSUP  # epilogue
+    assert f(A + 4, B, C, D, 64, 64, 64, 0, None, 0, E, None) == ALIGN
+    assert f(A, B, C, D, 64, 64, 64, 0, None, 0, A + 16, None) == ALIAS
+    i = L.tfq_scaled_mm_int8
+    assert i(A, B, C, D, 64, 64, 64, None, 0, None, None, None) == NULL
+    assert i(A, B, C, D, 64, 64, 131072, None, 0, E, None, None) == SHAPE  # INT32 bound
+    assert i(A, B, C, D, 64, 64, 64, None, 0, E, E + 64, None) == ALIAS    # y over acc
+
+
+@no_gpu_only
+def test_fused_validation(L):
+    ws = L.tfq_quant_linear_workspace_bytes
+    need = ws(100, 256, 0, 0)
+    assert need == 25600 + 400  # codes (256-aligned) + scales
+    assert ws(100, 256, 0, 128) == 25600 + 100 * 2 * 4
+    assert ws(100, 256, 1, 128) == 0 and ws(0, 256, 0, 0) == 0 and ws(100, 250, 0, 0) == 0
+    fu = L.tfq_quant_linear_fused
+    assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, E, need - 1, None) == WS
+    assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, E + 16, need, None) == ALIGN
+    assert fu(A, 100, 256, 256, B, C, 64, 0, 449.0, 0, None, 0, D, E, need, None) == QMAX
+    assert fu(A, 100, 256, 256, B, C, 64, 1, 127.0, 128, None, 0, D, E, need, None) == UNSUP
+    assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, A, need, None) == ALIAS
+    assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, A + 256, E, need, None) == ALIAS
+
+
+@no_gpu_only
+def test_valid_call_without_gpu_reports_device(L):
+    # everything valid: the only thing missing is a gfx950
+    assert L.tfq_quantize_rows(A, 4, 64, 64, 0, 448.0, 0, B, C, None) == DEV
+    assert L.tfq_scaled_mm_fp8(A, B, C, D, 64, 64, 64, 0, None, 0, E, None) == DEV
+    assert L.tfq_e4m3fn_encode_f32(A, B, 64, None) == DEV
+
+
+def test_python_binding_names_match_abi():
+    import int8_w8a8_quantized_amd as P
+
+    for n in declared_functions():
+        if n in ("tfq_status_string", "tfq_last_hip_error"):
+            continue
+        assert callable(getattr(P, n)), n
