@@ -18,8 +18,8 @@
 //    registers while the MFMAs of the current K step run, double-buffered
 //    LDS (2 x 64 KB of the 160 KB), one barrier per K step;
 //  * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
-//    the row's low 3 bits so that the MFMA fragment reads (16 rows x 16 B per
-//    8 lanes) hit distinct banks;
+//    (row >> 1) & 7 so that the MFMA fragment reads (16 consecutive rows at
+//    one chunk, served 16 lanes per cycle from 64 banks) hit distinct banks;
 //  * the K order inside an MFMA is irrelevant to the sum as long as A and B
 //    use the same one, so each lane group simply reads 32 contiguous bytes;
 //  * tile order: consecutive workgroup ids go round-robin over the 8 XCDs,
@@ -136,12 +136,12 @@ void scaled_gemm_kernel(const Params p)
     const int cc = t & 7, rr = t >> 3;
     const int voff = rr * K + cc * 16;
     const int row_stride32 = 32 * K;
-    const int lds_w = rr * BK + ((cc ^ (rr & 7)) << 4);
+    const int lds_w = rr * BK + ((cc ^ ((rr >> 1) & 7)) << 4);
 
     // LDS -> MFMA fragments: lane reads row (lane & 15), bytes [32 g, 32 g + 32)
     const int fr = lane & 15, g = lane >> 4;
-    const int rd0 = fr * BK + (((2 * g) ^ (lane & 7)) << 4);
-    const int rd1 = fr * BK + (((2 * g + 1) ^ (lane & 7)) << 4);
+    const int rd0 = fr * BK + (((2 * g) ^ ((fr >> 1) & 7)) << 4);
+    const int rd1 = fr * BK + (((2 * g + 1) ^ ((fr >> 1) & 7)) << 4);
     const int a_rd = wm * 128 * BK;
     const int b_rd = A_BYTES + wn * 128 * BK;
 
@@ -283,6 +283,274 @@ void scaled_gemm_kernel(const Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel for per-token / per-channel scales.  64 K-bytes per stage;
+// a ring of 4 register stages of 128-bit buffer loads keeps 3 stages of
+// global loads in flight (the compiler tracks them with exact vmcnt waits),
+// 2 LDS buffers, one barrier per stage; 4 waves x (128 x 128) with
+// v_mfma_f32_32x32x64_f8f6f4 (FP8) or 2x v_mfma_i32_32x32x32_i8 (INT8).
+// ---------------------------------------------------------------------------
+constexpr int PK = 64;                // K bytes per stage
+constexpr int PD = 4;                 // register stages in the ring
+constexpr int PA = BM * PK;           // 16 KB of A per stage
+constexpr int PSTAGE = PA + BN * PK;  // 32 KB per LDS buffer
+constexpr int EPITCH = 272;           // bytes per staged output row (256 + 16)
+constexpr int PSMEM = (2 * PSTAGE > 4 * 128 * EPITCH) ? 2 * PSTAGE : 4 * 128 * EPITCH;
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// all of this wave's LDS operations are complete, then a workgroup barrier
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int QT>
+struct PipeAcc;
+template <>
+struct PipeAcc<kE4M3FN> {
+    typedef v16f type;
+};
+template <>
+struct PipeAcc<kInt8> {
+    typedef v16i type;
+};
+
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_pipe_kernel(const Params p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[PSMEM];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = p.k;
+    const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+
+    // global -> registers: chunk (t & 3) of rows (t >> 2) + 64 j, j = 0..3, of A and B
+    const int lc = t & 3, lr = t >> 2;
+    const int voff = lr * K + lc * 16;
+    const int stride64 = 64 * K;
+    // registers -> LDS: 64-byte rows, 16-byte chunk index XOR ((row >> 2) & 3).
+    // The LDS serves a ds_read_b128 16 lanes per cycle from 64 banks; the 16
+    // lanes read 16 consecutive rows at one logical chunk, and this swizzle
+    // puts them in 16 different 16-byte bank groups (the writes, 4 rows x 4
+    // chunks per 16 lanes, are conflict-free too).
+    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
+    // LDS -> fragments: lane reads row (lane & 31), bytes [32 h, 32 h + 32)
+    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
+    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
+    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
+    const int a_rd = wm * 128 * PK;
+    const int b_rd = PA + wn * 128 * PK;
+    const int KT = (K + PK - 1) / PK;
+
+    v4u ga[PD][4], gb[PD][4];
+    typedef typename PipeAcc<QT>::type acc_t;
+    acc_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+    // Loads past the end of K (the K tail and the padding stages up to a
+    // multiple of 4) get bit 31 set in their offset: out of range, they read
+    // zeros.  Keeping this branch-free lets the compiler count the loads in
+    // flight exactly.
+    auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[4]) {
+        const int k0 = kt * PK;
+        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = (voff + j * stride64 + k0) | oob;
+            da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        }
+    };
+    auto lstore = [&](int buf, const v4u (&da)[4], const v4u (&db)[4]) {
+        uint8_t* s = smem + buf * PSTAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
+            *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+        }
+    };
+    // fragment reads: B fragments of all 4 column tiles, A fragment of row tile mi
+    auto read_b = [&](int buf, v8i (&bf)[4]) {
+        const uint8_t* s = smem + buf * PSTAGE;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const v4i lo = *reinterpret_cast<const v4i*>(s + b_rd + ni * 32 * PK + rd0);
+            const v4i hi = *reinterpret_cast<const v4i*>(s + b_rd + ni * 32 * PK + rd1);
+            bf[ni] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+    auto read_a = [&](int buf, int mi) -> v8i {
+        const uint8_t* s = smem + buf * PSTAGE;
+        const v4i lo = *reinterpret_cast<const v4i*>(s + a_rd + mi * 32 * PK + rd0);
+        const v4i hi = *reinterpret_cast<const v4i*>(s + a_rd + mi * 32 * PK + rd1);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto mfma_row = [&](int mi, const v8i& af, const v8i (&bf)[4]) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            // weights as the first operand: the 32x32 result is the transposed
+            // output tile, so each lane ends up with 4 consecutive columns
+            if constexpr (QT == kE4M3FN) {
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[ni], af, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+            } else {
+                const v8i b8 = bf[ni];
+                acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{af[0], af[1], af[2], af[3]}, acc[mi][ni],
+                    0, 0, 0);
+                acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{af[4], af[5], af[6], af[7]}, acc[mi][ni],
+                    0, 0, 0);
+            }
+        }
+    };
+
+    // Prologue: stages 0..3 in flight, stage 0 in LDS buffer 0 and its first
+    // fragments in registers.  The loop runs a multiple of 4 stages; stages
+    // past K hold zeros.
+    v8i bfr[2][4];
+    v8i a0[2];
+#pragma unroll
+    for (int u = 0; u < PD; ++u) gload(u, ga[u], gb[u]);
+    lstore(0, ga[0], gb[0]);
+    lds_barrier();
+    read_b(0, bfr[0]);
+    a0[0] = read_a(0, 0);
+
+    // One stage s = kt + U (ring slot U, LDS buffer U % 2):
+    //  - write stage s+1 from its ring slot into the other LDS buffer (all
+    //    waves finished reading that buffer before the previous barrier);
+    //  - refill ring slot U with the loads of stage s+4;
+    //  - MFMAs of row tiles 0..2, reading the next A fragment ahead;
+    //  - barrier: stage s+1 is in LDS and nobody reads stage s any more;
+    //  - read stage s+1's first fragments while row tile 3's MFMAs run.
+#define TFQ_PIPE_STEP(U)                                                       \
+    {                                                                          \
+        constexpr int cur = (U) & 1, nxt = cur ^ 1;                            \
+        lstore(nxt, ga[((U) + 1) % PD], gb[((U) + 1) % PD]);                   \
+        gload(kt + (U) + PD, ga[(U)], gb[(U)]);                                \
+        v8i a_cur = a0[cur];                                                   \
+        _Pragma("unroll") for (int mi = 0; mi < 3; ++mi) {                     \
+            const v8i a_nx = read_a(cur, mi + 1);                              \
+            mfma_row(mi, a_cur, bfr[cur]);                                     \
+            a_cur = a_nx;                                                      \
+        }                                                                      \
+        lds_barrier();                                                         \
+        read_b(nxt, bfr[nxt]);                                                 \
+        a0[nxt] = read_a(nxt, 0);                                              \
+        mfma_row(3, a_cur, bfr[cur]);                                          \
+    }
+    for (int kt = 0; kt < KT; kt += PD) {
+        TFQ_PIPE_STEP(0)
+        TFQ_PIPE_STEP(1)
+        TFQ_PIPE_STEP(2)
+        TFQ_PIPE_STEP(3)
+    }
+#undef TFQ_PIPE_STEP
+
+    // ---- epilogue ----
+    // With the weights as the first MFMA operand, lane (fr, h) holds, for row
+    // tile mi and column tile ni, output row  wm*128 + mi*32 + fr  and the
+    // four consecutive output columns  wn*128 + ni*32 + 8q + 4h + (0..3)  in
+    // registers 4q..4q+3 (q = 0..3).
+    float srow[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + fr;
+        srow[mi] = row < p.m ? p.sa[row] : 0.0f;
+    }
+    if constexpr (WANT_ACC) {
+        // raw INT32 sums: 16-byte stores of 4 consecutive columns
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int row = m0 + wm * 128 + mi * 32 + fr;
+            if (row >= p.m) continue;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = n0 + wn * 128 + ni * 32 + 8 * q + 4 * h;
+                    if (c0 < p.n)
+                        *reinterpret_cast<v4i*>(p.acc + (int64_t)row * p.n + c0) =
+                            v4i{(int)acc[mi][ni][4 * q], (int)acc[mi][ni][4 * q + 1],
+                                (int)acc[mi][ni][4 * q + 2], (int)acc[mi][ni][4 * q + 3]};
+                }
+        }
+    }
+    if constexpr (WANT_Y) {
+        // BF16 results are staged per wave in LDS (128 rows x 256 bytes, rows
+        // padded to 272 bytes) and written back as whole 256-byte row segments
+        // with 16-byte stores.
+        lds_barrier();  // every wave is done with the pipeline buffers
+        uint8_t* stg = smem + wave * 128 * EPITCH;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = n0 + wn * 128 + ni * 32 + 8 * q + 4 * h;
+                float sc[4], bc[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = c0 + j < p.n;
+                    sc[j] = ok ? p.sb[c0 + j] : 0.0f;
+                    bc[j] = (p.bias != nullptr && ok) ? bf16_to_f32(p.bias[c0 + j]) : 0.0f;
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[j]);
+                        if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
+                        if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH +
+                                              (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+                }
+            }
+        }
+        // the wave reads back only what it wrote itself
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int ch = lane & 15;
+        const int gcol = n0 + wn * 128 + ch * 8;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int lrow = j * 4 + (lane >> 4);
+            const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * EPITCH + ch * 16);
+            const int grow = m0 + wm * 128 + lrow;
+            if (grow < p.m && gcol < p.n)
+                *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
+        }
+    }
+}
+
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+hipError_t launch_pipe(const Params& p, hipStream_t st)
+{
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC>), dim3(grid), dim3(256), 0, st,
+                       p);
+    return hipGetLastError();
+}
+
 template <int QT, bool BLOCK, int EPI, bool WANT_Y, bool WANT_ACC>
 hipError_t launch_one(const Params& p, hipStream_t st)
 {
@@ -313,18 +581,18 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
         if (g.scale_block == 128)
             return g.epi == 1 ? launch_one<kE4M3FN, true, 1, true, false>(p, stream)
                               : launch_one<kE4M3FN, true, 0, true, false>(p, stream);
-        return g.epi == 1 ? launch_one<kE4M3FN, false, 1, true, false>(p, stream)
-                          : launch_one<kE4M3FN, false, 0, true, false>(p, stream);
+        return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false>(p, stream)
+                          : launch_pipe<kE4M3FN, 0, true, false>(p, stream);
     }
     const bool y = g.y != nullptr, a = g.acc != nullptr;
     if (g.epi == 1) {
-        if (y && a) return launch_one<kInt8, false, 1, true, true>(p, stream);
-        if (y) return launch_one<kInt8, false, 1, true, false>(p, stream);
-        return launch_one<kInt8, false, 1, false, true>(p, stream);
+        if (y && a) return launch_pipe<kInt8, 1, true, true>(p, stream);
+        if (y) return launch_pipe<kInt8, 1, true, false>(p, stream);
+        return launch_pipe<kInt8, 1, false, true>(p, stream);
     }
-    if (y && a) return launch_one<kInt8, false, 0, true, true>(p, stream);
-    if (y) return launch_one<kInt8, false, 0, true, false>(p, stream);
-    return launch_one<kInt8, false, 0, false, true>(p, stream);
+    if (y && a) return launch_pipe<kInt8, 0, true, true>(p, stream);
+    if (y) return launch_pipe<kInt8, 0, true, false>(p, stream);
+    return launch_pipe<kInt8, 0, false, true>(p, stream);
 }
 
 }  // namespace tfq
