@@ -67,6 +67,23 @@ class EventTimer:
         self.pairs.clear()
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record, or None when the GEMM source has changed since it was taken."""
+    import hashlib
+
+    rec_path = os.path.join(ROOT, "profiles", "traffic_video_dit_ffn_pair.json")
+    src = os.path.join(ROOT, "int8_w8a8_quantized_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(rec_path))
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["gemm_source_sha256"]:
+            return None
+        r = rec[kernel]
+        return int(r["read_bytes"] + r["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def quant_bytes(m, k, group=0):
     return 3 * m * k + 4 * m * (k // group if group else 1)
 
@@ -187,6 +204,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy three times (the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -201,6 +221,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB three times")
+        return
 
     log("generating c4_video_dit inputs (seeded synthetic)")
     t0 = time.perf_counter()
@@ -255,7 +283,9 @@ def main():
     achieved = up_flops / (per["gemm_up_gelu"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "scaled_gemm fp8 (up projection + GELU epilogue)",
                 "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("gemm_up_gelu"),
+                "algorithmic_bytes": M * K + N * K + 4 * M + 4 * N + 2 * M * N}
     kernels = {
         "quant_x": {"ms": per["quant_x"], "gbs": quant_bytes(M, K) / per["quant_x"] / 1e6},
         "gemm_up_gelu": {"ms": per["gemm_up_gelu"], "tflops": achieved},
