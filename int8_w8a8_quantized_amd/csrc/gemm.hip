@@ -8,27 +8,25 @@
 // 1x128 activation group and per 128x128 weight block, applied per K-block.
 //
 // Design (MI355X):
-//  * both operands are K-contiguous ("TN"), the layout the MFMA operands want;
-//  * 256x256 output tile per workgroup, 4 waves in a 2x2 grid, 128x128 per
-//    wave = 8x8 v_mfma_f32_16x16x128_f8f6f4 (FP8) or 2x 8x8
-//    v_mfma_i32_16x16x64_i8 (INT8) per 128-deep K step; accumulators live in
-//    the AGPR half of the 512-entry register file (one wave per SIMD);
-//  * global -> LDS through 128-bit buffer loads (out-of-range rows and the K
-//    tail read as zero, so ragged M/N/K need no extra branches), staged in
-//    registers while the MFMAs of the current K step run, double-buffered
-//    LDS (2 x 64 KB of the 160 KB), one barrier per K step;
-//  * LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
-//    (row >> 1) & 7 so that the MFMA fragment reads (16 consecutive rows at
-//    one chunk, served 16 lanes per cycle from 64 banks) hit distinct banks;
-//  * the K order inside an MFMA is irrelevant to the sum as long as A and B
-//    use the same one, so each lane group simply reads 32 contiguous bytes;
+//  * both operands are K-contiguous ("TN"), the layout MFMA operands want;
+//  * the K order inside an MFMA does not change the sum as long as A and B
+//    use the same one, so each lane group reads 32 contiguous bytes;
+//  * global -> registers through 128-bit buffer loads (out-of-range rows and
+//    the K tail read as zero, so ragged M/N/K need no branches), a ring of
+//    register stages keeps several K stages of loads in flight while MFMAs
+//    run, then registers -> LDS (64-byte rows, chunk swizzled to be free of
+//    bank conflicts) -> MFMA fragments;
+//  * the weights are the first MFMA operand, so each lane finishes with four
+//    consecutive output columns of one row; the epilogue scales in FP32,
+//    stages BF16 rows in LDS and writes whole row segments with 16-byte
+//    stores;
 //  * tile order: consecutive workgroup ids go round-robin over the 8 XCDs,
 //    so ids are remapped to give each XCD a contiguous slice of the tile
-//    sequence, and the sequence walks bands of 8 tile rows so that the 32
-//    tiles in flight on one XCD share A and B panels in that XCD's L2;
-//  * epilogue: FP32 (acc * s_a) * s_b [+ bias] [GELU-tanh] -> BF16 (RNE); the
-//    INT8 path converts the exact INT32 sum to FP32 first and rounds each
-//    product in a fixed order (bit-reproducible); raw INT32 output is optional.
+//    sequence, which walks bands of 8 tile rows so that the tiles in flight
+//    on one XCD share A and B panels in that XCD's L2;
+//  * epilogue arithmetic: FP32 (acc * s_a) * s_b [+ bias] [GELU-tanh] -> BF16
+//    (RNE), each step rounded on its own; the INT8 path converts the exact
+//    INT32 sum to FP32 first (bit-reproducible); raw INT32 output optional.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
@@ -45,11 +43,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int A_BYTES = BM * BK;                 // 32 KB
-constexpr int B_BYTES = BN * BK;                 // 32 KB
-constexpr int SA_BYTES = BM * 4;                 // block-mode activation scales of one K step
-constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+constexpr int BM = 256, BN = 256;  // output tile of the per-token / per-channel kernel
 constexpr int GROUP_M = 8;
 
 struct Params {
@@ -111,176 +105,6 @@ __device__ __forceinline__ float gelu_tanh(float h)
     const float z = h * __builtin_fmaf(c2, h * h, c1);
     const float e = __builtin_amdgcn_exp2f(z);
     return h * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-template <int QT, bool BLOCK, int EPI, bool WANT_Y, bool WANT_ACC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void scaled_gemm_kernel(const Params p)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int K = p.k;
-    const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
-
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
-
-    // global -> LDS: thread t moves chunk (t & 7) of rows (t >> 3) + 32 j
-    const int cc = t & 7, rr = t >> 3;
-    const int voff = rr * K + cc * 16;
-    const int row_stride32 = 32 * K;
-    const int lds_w = rr * BK + ((cc ^ ((rr >> 1) & 7)) << 4);
-
-    // LDS -> MFMA fragments: lane reads row (lane & 15), bytes [32 g, 32 g + 32)
-    const int fr = lane & 15, g = lane >> 4;
-    const int rd0 = fr * BK + (((2 * g) ^ ((fr >> 1) & 7)) << 4);
-    const int rd1 = fr * BK + (((2 * g + 1) ^ ((fr >> 1) & 7)) << 4);
-    const int a_rd = wm * 128 * BK;
-    const int b_rd = A_BYTES + wn * 128 * BK;
-
-    const int KT = (K + BK - 1) / BK;
-
-    v4u ga[8], gb[8];
-    float gs = 0.0f;  // block mode: this thread's activation scale of the next K step
-    const int kblocks = K >> 7;
-
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK;
-        const bool kin = (k0 + cc * 16) < K;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int off = kin ? voff + j * row_stride32 + k0 : (int)0x80000000;
-            ga[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-            gb[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        }
-        if constexpr (BLOCK) gs = (t < rows_a) ? p.sa[(int64_t)(m0 + t) * kblocks + kt] : 0.0f;
-    };
-    auto lstore = [&](int stage) {
-        uint8_t* s = smem + stage * STAGE;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<v4u*>(s + lds_w + j * 32 * BK) = ga[j];
-            *reinterpret_cast<v4u*>(s + A_BYTES + lds_w + j * 32 * BK) = gb[j];
-        }
-        if constexpr (BLOCK) reinterpret_cast<float*>(s + A_BYTES + B_BYTES)[t] = gs;
-    };
-
-    typedef typename std::conditional<QT == kE4M3FN, v4f, v4i>::type acc_t;
-    acc_t acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        const uint8_t* s = smem + cur * STAGE;
-
-        v8i bf[8];
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-            const v4i lo = *reinterpret_cast<const v4i*>(s + b_rd + ni * 16 * BK + rd0);
-            const v4i hi = *reinterpret_cast<const v4i*>(s + b_rd + ni * 16 * BK + rd1);
-            bf[ni] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        float sbk = 0.0f;
-        if constexpr (BLOCK) {
-            const int nb = (n0 + wn * 128) >> 7;
-            sbk = (n0 + wn * 128 < p.n) ? p.sb[(int64_t)nb * kblocks + kt] : 0.0f;
-        }
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            const v4i lo = *reinterpret_cast<const v4i*>(s + a_rd + mi * 16 * BK + rd0);
-            const v4i hi = *reinterpret_cast<const v4i*>(s + a_rd + mi * 16 * BK + rd1);
-            if constexpr (QT == kE4M3FN) {
-                const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                if constexpr (!BLOCK) {
-#pragma unroll
-                    for (int ni = 0; ni < 8; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af, bf[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
-                } else {
-                    // this lane's 4 rows of the mi-th 16-row slab
-                    const v4f sr = *reinterpret_cast<const v4f*>(
-                        s + A_BYTES + B_BYTES + (wm * 128 + mi * 16 + 4 * g) * 4);
-                    const v4f f = sr * sbk;
-#pragma unroll
-                    for (int ni = 0; ni < 8; ++ni) {
-                        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af, bf[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[mi][ni][r] = __builtin_fmaf(part[r], f[r], acc[mi][ni][r]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
-                    const v8i b8 = bf[ni];
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        lo, v4i{b8[0], b8[1], b8[2], b8[3]}, acc[mi][ni], 0, 0, 0);
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                        hi, v4i{b8[4], b8[5], b8[6], b8[7]}, acc[mi][ni], 0, 0, 0);
-                }
-            }
-        }
-        if (kt + 1 < KT) lstore(cur ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue ----
-    // MFMA 16x16 output layout: lane holds rows 4*(lane>>4) + r (r = 0..3) of
-    // column (lane & 15) of each 16x16 tile.
-    float scol[8], bcol[8];
-    int col[8];
-#pragma unroll
-    for (int ni = 0; ni < 8; ++ni) {
-        col[ni] = n0 + wn * 128 + ni * 16 + fr;
-        const bool ok = col[ni] < p.n;
-        if constexpr (!BLOCK) scol[ni] = ok ? p.sb[col[ni]] : 0.0f;
-        bcol[ni] = (p.bias != nullptr && ok) ? bf16_to_f32(p.bias[col[ni]]) : 0.0f;
-    }
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * 128 + mi * 16 + 4 * g + r;
-            if (row >= p.m) continue;
-            float srow = 1.0f;
-            if constexpr (!BLOCK) srow = p.sa[row];
-            uint16_t* yr = WANT_Y ? p.y + (int64_t)row * p.n : nullptr;
-            int32_t* ar = WANT_ACC ? p.acc + (int64_t)row * p.n : nullptr;
-#pragma unroll
-            for (int ni = 0; ni < 8; ++ni) {
-                if (col[ni] >= p.n) continue;
-                if constexpr (WANT_ACC) ar[col[ni]] = acc[mi][ni][r];
-                if constexpr (WANT_Y) {
-                    float v;
-                    if constexpr (QT == kE4M3FN) {
-                        if constexpr (BLOCK) v = acc[mi][ni][r];
-                        else v = scale_out(acc[mi][ni][r], srow, scol[ni]);
-                    } else {
-                        v = scale_out((float)acc[mi][ni][r], srow, scol[ni]);
-                    }
-                    if (p.bias != nullptr) v = add_bias(v, bcol[ni]);
-                    if constexpr (EPI == 1) v = gelu_tanh(v);
-                    yr[col[ni]] = f32_to_bf16(v);
-                }
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -542,21 +366,198 @@ void gemm_pipe_kernel(const Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-scaled FP8 kernel: 1x128 activation groups and 128x128 weight blocks
+// (LightX2V "模型量化技术", table "量化模式", fp8-b128-deepgemm).  256x128
+// output tile, 4 waves (2x2) of 128x64, so every wave's 64 columns lie in one
+// 128-wide weight block and -- with the weights as the first MFMA operand --
+// every lane's output row is fixed per 32-row tile: the scale of a
+// (row, K-block) pair is one float per row tile.  Each 128-deep K block is
+// two 64-deep stages whose MFMAs accumulate into a temporary; then
+// acc += temp * (s_a[row, kb] * s_b[nb, kb]).  Same register-staged pipeline
+// as gemm_pipe_kernel with a 2-stage ring.
+// ---------------------------------------------------------------------------
+constexpr int QBN = 128;                   // output columns per workgroup
+constexpr int QSTAGE = PA + QBN * PK;      // 24 KB per LDS buffer
+constexpr int QEPITCH = 144;               // staged output row: 64 columns * 2 B + 16
+constexpr int QSMEM = (2 * QSTAGE > 4 * 128 * QEPITCH) ? 2 * QSTAGE : 4 * 128 * QEPITCH;
+constexpr int QD = 2;                      // register stages in the ring
+
+template <int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_block_kernel(const Params p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[QSMEM];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * QBN;
+    const int K = p.k;
+    const int kblocks = K >> 7;
+    const int rows_a = min(BM, p.m - m0), rows_b = min(QBN, p.n - n0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+
+    // global -> registers: chunk (t & 3) of A rows (t >> 2) + 64 j (j < 4) and
+    // of B rows (t >> 2) + 64 j (j < 2)
+    const int lc = t & 3, lr = t >> 2;
+    const int voff = lr * K + lc * 16;
+    const int stride64 = 64 * K;
+    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
+    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
+    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
+    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
+    const int a_rd = wm * 128 * PK;
+    const int b_rd = PA + wn * 64 * PK;
+    const int KT = K / PK;  // even: K % 128 == 0
+
+    v4u ga[QD][4], gb[QD][2];
+    v16f acc[4][2], tmp[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[2]) {
+        const int k0 = kt * PK;
+        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = (voff + j * stride64 + k0) | oob;
+            da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            if (j < 2) db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        }
+    };
+    auto lstore = [&](int buf, const v4u (&da)[4], const v4u (&db)[2]) {
+        uint8_t* s = smem + buf * QSTAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
+            if (j < 2) *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+        }
+    };
+    auto frag = [&](const uint8_t* s) -> v8i {
+        const v4i lo = *reinterpret_cast<const v4i*>(s + rd0);
+        const v4i hi = *reinterpret_cast<const v4i*>(s + rd1);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // this lane's output rows (one per 32-row tile) and the K-block scale factors
+    int arow[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) arow[mi] = m0 + wm * 128 + mi * 32 + fr;
+    const int nb = (n0 + wn * 64) >> 7;
+    const bool col_ok = n0 + wn * 64 < p.n;
+    auto block_scales = [&](int kb, float (&f)[4]) {
+        const float sb = col_ok ? p.sb[(int64_t)nb * kblocks + kb] : 0.0f;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            f[mi] = (arow[mi] < p.m ? p.sa[(int64_t)arow[mi] * kblocks + kb] : 0.0f) * sb;
+    };
+    // one 64-deep stage of MFMAs into the temporaries (first half of a block
+    // starts them from zero)
+    auto compute = [&](int buf, bool first) {
+        const uint8_t* s = smem + buf * QSTAGE;
+        v8i bf[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * PK);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const v8i af = frag(s + a_rd + mi * 32 * PK);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                tmp[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[ni], af, first ? v16f{} : tmp[mi][ni], 0, 0, 0, 0, 0, 0);
+        }
+    };
+
+    gload(0, ga[0], gb[0]);
+    gload(1, ga[1], gb[1]);
+    lstore(0, ga[0], gb[0]);
+    float f[4];
+    // stage s = kt + U: ring slot U, LDS buffer U; U = 0 is the first half of
+    // K block kt/2, U = 1 its second half
+    for (int kt = 0; kt < KT; kt += 2) {
+        lds_barrier();
+        lstore(1, ga[1], gb[1]);
+        gload(kt + 2, ga[0], gb[0]);
+        block_scales(kt >> 1, f);
+        compute(0, true);
+        lds_barrier();
+        lstore(0, ga[0], gb[0]);
+        gload(kt + 3, ga[1], gb[1]);
+        compute(1, false);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[mi][ni][e] = __builtin_fmaf(tmp[mi][ni][e], f[mi], acc[mi][ni][e]);
+    }
+
+    // ---- epilogue: lane holds row arow[mi] and columns
+    // wn*64 + ni*32 + 8q + 4h + (0..3) in registers 4q..4q+3 ----
+    lds_barrier();
+    uint8_t* stg = smem + wave * 128 * QEPITCH;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c0 = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
+            float bc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bc[j] = (p.bias != nullptr && c0 + j < p.n) ? bf16_to_f32(p.bias[c0 + j]) : 0.0f;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = acc[mi][ni][4 * q + j];
+                    if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
+                    if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                }
+                const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH +
+                                          (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int ch = lane & 7;
+    const int gcol = n0 + wn * 64 + ch * 8;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int lrow = j * 8 + (lane >> 3);
+        const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * QEPITCH + ch * 16);
+        const int grow = m0 + wm * 128 + lrow;
+        if (grow < p.m && gcol < p.n)
+            *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
+    }
+}
+
+template <int EPI>
+hipError_t launch_block(Params p, hipStream_t st)
+{
+    p.tiles_n = (p.n + QBN - 1) / QBN;
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    hipLaunchKernelGGL((gemm_block_kernel<EPI>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
 hipError_t launch_pipe(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
     hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC>), dim3(grid), dim3(256), 0, st,
                        p);
-    return hipGetLastError();
-}
-
-template <int QT, bool BLOCK, int EPI, bool WANT_Y, bool WANT_ACC>
-hipError_t launch_one(const Params& p, hipStream_t st)
-{
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    hipLaunchKernelGGL((scaled_gemm_kernel<QT, BLOCK, EPI, WANT_Y, WANT_ACC>), dim3(grid),
-                       dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -579,8 +580,7 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.tiles_n = (int)((g.n + BN - 1) / BN);
     if (g.qtype == kE4M3FN) {
         if (g.scale_block == 128)
-            return g.epi == 1 ? launch_one<kE4M3FN, true, 1, true, false>(p, stream)
-                              : launch_one<kE4M3FN, true, 0, true, false>(p, stream);
+            return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
         return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false>(p, stream)
                           : launch_pipe<kE4M3FN, 0, true, false>(p, stream);
     }
