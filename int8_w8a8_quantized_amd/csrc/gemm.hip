@@ -22,7 +22,7 @@
 //    stores;
 //  * tile order: consecutive workgroup ids go round-robin over the 8 XCDs,
 //    so ids are remapped to give each XCD a contiguous slice of the tile
-//    sequence, which walks bands of 8 tile rows so that the tiles in flight
+//    sequence, which walks bands of 4 tile rows so that the tiles in flight
 //    on one XCD share A and B panels in that XCD's L2;
 //  * epilogue arithmetic: FP32 (acc * s_a) * s_b [+ bias] [GELU-tanh] -> BF16
 //    (RNE), each step rounded on its own; the INT8 path converts the exact
@@ -44,7 +44,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;  // output tile of the per-token / per-channel kernel
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 
 struct Params {
     const uint8_t* a;
@@ -381,7 +381,8 @@ constexpr int QBN = 128;                   // output columns per workgroup
 constexpr int QSTAGE = PA + QBN * PK;      // 24 KB per LDS buffer
 constexpr int QEPITCH = 144;               // staged output row: 64 columns * 2 B + 16
 constexpr int QSMEM = (2 * QSTAGE > 4 * 128 * QEPITCH) ? 2 * QSTAGE : 4 * 128 * QEPITCH;
-constexpr int QD = 2;                      // register stages in the ring
+constexpr int QD = 2;                      // register stages in the block kernel's ring
+constexpr int DSMEM = (3 * QSTAGE > 4 * 128 * QEPITCH) ? 3 * QSTAGE : 4 * 128 * QEPITCH;
 
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -543,6 +544,205 @@ void gemm_block_kernel(const Params p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two-workgroups-per-CU kernel for per-token / per-channel scales: the
+// block kernel's 256x128 tile and 4 waves of 128x64, with at most 256
+// registers per wave and 72 KB of LDS per workgroup so that two workgroups
+// share every CU; each SIMD then interleaves the MFMAs of two independent
+// waves, which hides one workgroup's barrier and memory waits behind the
+// other's MFMAs.
+// ---------------------------------------------------------------------------
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void gemm_dual_kernel(const Params p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DSMEM];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * QBN;
+    const int K = p.k;
+    const int rows_a = min(BM, p.m - m0), rows_b = min(QBN, p.n - n0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+
+    const int lc = t & 3, lr = t >> 2;
+    const int voff = lr * K + lc * 16;
+    const int stride64 = 64 * K;
+    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
+    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
+    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
+    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
+    const int a_rd = wm * 128 * PK;
+    const int b_rd = PA + wn * 64 * PK;
+    const int KT = (K + PK - 1) / PK;
+
+    typedef typename PipeAcc<QT>::type acc_t;
+    v4u ga[3][4], gb[3][2];
+    acc_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+    auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[2]) {
+        const int k0 = kt * PK;
+        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = (voff + j * stride64 + k0) | oob;
+            da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            if (j < 2) db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        }
+    };
+    auto lstore = [&](int buf, const v4u (&da)[4], const v4u (&db)[2]) {
+        uint8_t* s = smem + buf * QSTAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
+            if (j < 2) *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+        }
+    };
+    auto frag = [&](const uint8_t* s) -> v8i {
+        const v4i lo = *reinterpret_cast<const v4i*>(s + rd0);
+        const v4i hi = *reinterpret_cast<const v4i*>(s + rd1);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto compute = [&](int buf) {
+        const uint8_t* s = smem + buf * QSTAGE;
+        v8i bf[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * PK);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const v8i af = frag(s + a_rd + mi * 32 * PK);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                if constexpr (QT == kE4M3FN) {
+                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf[ni], af, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+                } else {
+                    const v8i b8 = bf[ni];
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{af[0], af[1], af[2], af[3]},
+                        acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{af[4], af[5], af[6], af[7]},
+                        acc[mi][ni], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // 3-slot register ring and 3 LDS buffers (stage s in slot and buffer
+    // s % 3), one barrier per stage: step s writes stage s+1 into the buffer
+    // of stage s-2, loads stage s+3 into the slot it just emptied and
+    // computes stage s.  The loop runs a multiple of 3 stages (stages past K
+    // read zeros).
+    gload(0, ga[0], gb[0]);
+    gload(1, ga[1], gb[1]);
+    gload(2, ga[2], gb[2]);
+    lstore(0, ga[0], gb[0]);
+#define TFQ_DUAL_STEP(U)                                                       \
+    {                                                                          \
+        lds_barrier();                                                         \
+        lstore(((U) + 1) % 3, ga[((U) + 1) % 3], gb[((U) + 1) % 3]);          \
+        gload(kt + (U) + 3, ga[(U)], gb[(U)]);                                 \
+        compute((U));                                                          \
+    }
+    for (int kt = 0; kt < KT; kt += 3) {
+        TFQ_DUAL_STEP(0)
+        TFQ_DUAL_STEP(1)
+        TFQ_DUAL_STEP(2)
+    }
+#undef TFQ_DUAL_STEP
+
+    // ---- epilogue: lane holds row wm*128 + mi*32 + fr and columns
+    // wn*64 + ni*32 + 8q + 4h + (0..3) in registers 4q..4q+3 ----
+    float srow[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + fr;
+        srow[mi] = row < p.m ? p.sa[row] : 0.0f;
+    }
+    if constexpr (WANT_ACC) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int row = m0 + wm * 128 + mi * 32 + fr;
+            if (row >= p.m) continue;
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
+                    if (c0 < p.n)
+                        *reinterpret_cast<v4i*>(p.acc + (int64_t)row * p.n + c0) =
+                            v4i{(int)acc[mi][ni][4 * q], (int)acc[mi][ni][4 * q + 1],
+                                (int)acc[mi][ni][4 * q + 2], (int)acc[mi][ni][4 * q + 3]};
+                }
+        }
+    }
+    if constexpr (WANT_Y) {
+        lds_barrier();
+        uint8_t* stg = smem + wave * 128 * QEPITCH;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
+                float sc[4], bc[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = c0 + j < p.n;
+                    sc[j] = ok ? p.sb[c0 + j] : 0.0f;
+                    bc[j] = (p.bias != nullptr && ok) ? bf16_to_f32(p.bias[c0 + j]) : 0.0f;
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[j]);
+                        if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
+                        if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH +
+                                              (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int ch = lane & 7;
+        const int gcol = n0 + wn * 64 + ch * 8;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int lrow = j * 8 + (lane >> 3);
+            const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * QEPITCH + ch * 16);
+            const int grow = m0 + wm * 128 + lrow;
+            if (grow < p.m && gcol < p.n)
+                *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
+        }
+    }
+}
+
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+hipError_t launch_dual(Params p, hipStream_t st)
+{
+    p.tiles_n = (p.n + QBN - 1) / QBN;
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    hipLaunchKernelGGL((gemm_dual_kernel<QT, EPI, WANT_Y, WANT_ACC>), dim3(grid), dim3(256), 0, st,
+                       p);
+    return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_block(Params p, hipStream_t st)
 {
@@ -578,13 +778,31 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.k = (int)g.k;
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
+    if (g.scale_block == 128)
+        return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
+    // Kernel choice by shape: with fewer 256x256 tiles than the 256 CUs the
+    // big-tile kernel leaves CUs idle, so the 256x128 two-per-CU kernel takes
+    // those problems.  Both sum every output in the same order (same MFMAs,
+    // same 64-deep K stages), so the choice never changes a result bit.
+    const bool dual = p.tiles_m * p.tiles_n < 256;
+    const bool y = g.y != nullptr, a = g.acc != nullptr;
     if (g.qtype == kE4M3FN) {
-        if (g.scale_block == 128)
-            return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
+        if (dual)
+            return g.epi == 1 ? launch_dual<kE4M3FN, 1, true, false>(p, stream)
+                              : launch_dual<kE4M3FN, 0, true, false>(p, stream);
         return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false>(p, stream)
                           : launch_pipe<kE4M3FN, 0, true, false>(p, stream);
     }
-    const bool y = g.y != nullptr, a = g.acc != nullptr;
+    if (dual) {
+        if (g.epi == 1) {
+            if (y && a) return launch_dual<kInt8, 1, true, true>(p, stream);
+            if (y) return launch_dual<kInt8, 1, true, false>(p, stream);
+            return launch_dual<kInt8, 1, false, true>(p, stream);
+        }
+        if (y && a) return launch_dual<kInt8, 0, true, true>(p, stream);
+        if (y) return launch_dual<kInt8, 0, true, false>(p, stream);
+        return launch_dual<kInt8, 0, false, true>(p, stream);
+    }
     if (g.epi == 1) {
         if (y && a) return launch_pipe<kInt8, 1, true, true>(p, stream);
         if (y) return launch_pipe<kInt8, 1, true, false>(p, stream);

@@ -164,3 +164,40 @@ def test_quant_linear_module_caches_weight(tfq):
     torch.cuda.synchronize()
     assert lin.w_q is wq_first
     assert torch.equal(y1, y2)
+
+
+def _sample_rows(M):
+    rng = np.random.default_rng(M)
+    return np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
+                                     rng.choice(np.arange(16, M - 16), 16, replace=False)]))
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+def test_big_tile_path_and_kernel_choice_invariance(tfq, qtype):
+    """A shape with more 256x256 tiles than CUs (M=4100, N=4104, ragged M, N
+    and K tails) runs the 256x256 kernel; its first 256 rows alone run the
+    256x128 two-per-CU kernel.  Sampled rows match the oracle and the
+    overlapping outputs of the two kernels are bit-identical."""
+    M, N, K = 4100, 4104, 336
+    _, _, qa, sa, qb, sb, _ = _operands(99, M, N, K, qtype)
+    dt = torch.uint8 if qtype == "fp8" else torch.int8
+    a, b = dev_u8(qa, dt), dev_u8(qb, dt)
+    sad, sbd = dev_f32(sa), dev_f32(sb)
+    say(f"big-tile path {qtype} M={M} N={N} K={K}")
+    if qtype == "fp8":
+        y = tfq.tfq_scaled_mm_fp8(a, sad, b, sbd)
+        y_small = tfq.tfq_scaled_mm_fp8(a[:256].contiguous(), sad[:256].contiguous(), b, sbd)
+    else:
+        y, acc = tfq.tfq_scaled_mm_int8(a, sad, b, sbd, want_y=True, want_acc=True)
+        y_small, _ = tfq.tfq_scaled_mm_int8(a[:256].contiguous(), sad[:256].contiguous(), b, sbd)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    yb = host_bits(y)
+    if qtype == "fp8":
+        ref = orc.linear_ref(qa, sa, qb, sb, "fp8", rows=rows)
+        assert_fp8_tolerance(yb[rows], ref, "big-tile fp8")
+    else:
+        acc_e, y_e = orc.int8_linear(qa, sa, qb, sb, rows=rows)
+        assert np.array_equal(host_bits(acc)[rows].astype(np.int64), acc_e)
+        assert np.array_equal(yb[rows], y_e)
+    assert np.array_equal(host_bits(y_small), yb[:256])
