@@ -119,7 +119,8 @@ constexpr int PD = 4;                 // register stages in the ring
 constexpr int PA = BM * PK;           // 16 KB of A per stage
 constexpr int PSTAGE = PA + BN * PK;  // 32 KB per LDS buffer
 constexpr int EPITCH = 272;           // bytes per staged output row (256 + 16)
-constexpr int PSMEM = (2 * PSTAGE > 4 * 128 * EPITCH) ? 2 * PSTAGE : 4 * 128 * EPITCH;
+constexpr int PBUF = 4;               // LDS buffers (one barrier per two stages)
+constexpr int PSMEM = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -245,48 +246,91 @@ void gemm_pipe_kernel(const Params p)
         }
     };
 
-    // Prologue: stages 0..3 in flight, stage 0 in LDS buffer 0 and its first
-    // fragments in registers.  The loop runs a multiple of 4 stages; stages
-    // past K hold zeros.
+    // one 16-byte chunk (A and B) of a ring slot: load, or write to LDS
+    auto gload_j = [&](int kt, v4u (&da)[4], v4u (&db)[4], int j) {
+        const int k0 = kt * PK;
+        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+        const int off = (voff + j * stride64 + k0) | oob;
+        da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+        db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    };
+    auto lstore_j = [&](int buf, const v4u (&da)[4], const v4u (&db)[4], int j) {
+        uint8_t* s = smem + buf * PSTAGE;
+        *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
+        *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+    };
+
+    // Stage s lives in ring slot s % 4 and LDS buffer s % 4.  Stages are
+    // processed in pairs with one barrier per pair: while pair (s, s+1) is
+    // computed, stages s+2 and s+3 move from their ring slots into the LDS
+    // buffers of s-2 and s-1 (free since the previous barrier) and the slots
+    // are refilled with stages s+6 and s+7 -- loads are issued 4 stages ahead.
+    // The barrier sits before the last row tile of stage s+1; stage s+2's
+    // first fragments are read while that row's MFMAs run.  Scheduling
+    // fences keep one chunk of LDS writes and loads between consecutive
+    // MFMA rows.  The loop runs a multiple of 4 stages (stages past K read
+    // zeros).
     v8i bfr[2][4];
     v8i a0[2];
 #pragma unroll
     for (int u = 0; u < PD; ++u) gload(u, ga[u], gb[u]);
     lstore(0, ga[0], gb[0]);
+    lstore(1, ga[1], gb[1]);
+    gload(4, ga[0], gb[0]);
+    gload(5, ga[1], gb[1]);
     lds_barrier();
     read_b(0, bfr[0]);
     a0[0] = read_a(0, 0);
 
-    // One stage s = kt + U (ring slot U, LDS buffer U % 2):
-    //  - write stage s+1 from its ring slot into the other LDS buffer (all
-    //    waves finished reading that buffer before the previous barrier);
-    //  - refill ring slot U with the loads of stage s+4;
-    //  - MFMAs of row tiles 0..2, reading the next A fragment ahead;
-    //  - barrier: stage s+1 is in LDS and nobody reads stage s any more;
-    //  - read stage s+1's first fragments while row tile 3's MFMAs run.
-#define TFQ_PIPE_STEP(U)                                                       \
-    {                                                                          \
-        constexpr int cur = (U) & 1, nxt = cur ^ 1;                            \
-        lstore(nxt, ga[((U) + 1) % PD], gb[((U) + 1) % PD]);                   \
-        gload(kt + (U) + PD, ga[(U)], gb[(U)]);                                \
-        v8i a_cur = a0[cur];                                                   \
-        _Pragma("unroll") for (int mi = 0; mi < 3; ++mi) {                     \
-            const v8i a_nx = read_a(cur, mi + 1);                              \
-            mfma_row(mi, a_cur, bfr[cur]);                                     \
-            a_cur = a_nx;                                                      \
-        }                                                                      \
-        lds_barrier();                                                         \
-        read_b(nxt, bfr[nxt]);                                                 \
-        a0[nxt] = read_a(nxt, 0);                                              \
-        mfma_row(3, a_cur, bfr[cur]);                                          \
-    }
+#define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
     for (int kt = 0; kt < KT; kt += PD) {
-        TFQ_PIPE_STEP(0)
-        TFQ_PIPE_STEP(1)
-        TFQ_PIPE_STEP(2)
-        TFQ_PIPE_STEP(3)
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+            const int b0 = 2 * P, b2 = (b0 + 2) & 3, b3 = (b0 + 3) & 3;
+            // first stage of the pair: buffer b0, fragments in set 0
+            {
+                read_b(b0 + 1, bfr[1]);
+                v8i a_cur = a0[0];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const v8i a_nx = read_a(mi < 3 ? b0 : b0 + 1, mi < 3 ? mi + 1 : 0);
+                    mfma_row(mi, a_cur, bfr[0]);
+                    TFQ_FENCE();
+                    lstore_j(b2, ga[b2], gb[b2], mi);
+                    gload_j(kt + b0 + 6, ga[b2], gb[b2], mi);
+                    TFQ_FENCE();
+                    a_cur = a_nx;
+                }
+                a0[1] = a_cur;
+            }
+            // second stage: buffer b0 + 1, fragments in set 1
+            {
+                v8i a_cur = a0[1];
+#pragma unroll
+                for (int mi = 0; mi < 3; ++mi) {
+                    const v8i a_nx = read_a(b0 + 1, mi + 1);
+                    mfma_row(mi, a_cur, bfr[1]);
+                    TFQ_FENCE();
+                    if (mi == 0) {
+                        lstore_j(b3, ga[b3], gb[b3], 0);
+                        gload_j(kt + b0 + 7, ga[b3], gb[b3], 0);
+                        lstore_j(b3, ga[b3], gb[b3], 1);
+                        gload_j(kt + b0 + 7, ga[b3], gb[b3], 1);
+                    } else {
+                        lstore_j(b3, ga[b3], gb[b3], mi + 1);
+                        gload_j(kt + b0 + 7, ga[b3], gb[b3], mi + 1);
+                    }
+                    TFQ_FENCE();
+                    a_cur = a_nx;
+                }
+                lds_barrier();
+                read_b(b2, bfr[0]);
+                a0[0] = read_a(b2, 0);
+                mfma_row(3, a_cur, bfr[1]);
+            }
+        }
     }
-#undef TFQ_PIPE_STEP
+#undef TFQ_FENCE
 
     // ---- epilogue ----
     // With the weights as the first MFMA operand, lane (fr, h) holds, for row
