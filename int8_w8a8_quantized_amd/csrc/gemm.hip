@@ -226,6 +226,20 @@ void gemm_pipe_kernel(const Params p)
         const v4i hi = *reinterpret_cast<const v4i*>(s + a_rd + mi * 32 * PK + rd1);
         return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
+    auto mfma_one = [&](int mi, int ni, const v8i& af, const v8i (&bf)[4]) {
+        if constexpr (QT == kE4M3FN) {
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[ni], af, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+        } else {
+            const v8i b8 = bf[ni];
+            acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{af[0], af[1], af[2], af[3]}, acc[mi][ni],
+                0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{af[4], af[5], af[6], af[7]}, acc[mi][ni],
+                0, 0, 0);
+        }
+    };
     auto mfma_row = [&](int mi, const v8i& af, const v8i (&bf)[4]) {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
@@ -258,6 +272,31 @@ void gemm_pipe_kernel(const Params p)
         uint8_t* s = smem + buf * PSTAGE;
         *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
         *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+    };
+    // one MFMA row with one memory operation after each MFMA:
+    // write A chunk j, write B chunk j, load A chunk j, load B chunk j
+    auto row_interleaved = [&](int mi, const v8i& af, const v8i (&bf)[4], int buf, v4u (&da)[4],
+                               v4u (&db)[4], int kt_load, int j) {
+        uint8_t* s = smem + buf * PSTAGE;
+        const int k0 = kt_load * PK;
+        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+        const int off = (voff + j * stride64 + k0) | oob;
+        mfma_one(mi, 0, af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_one(mi, 1, af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_one(mi, 2, af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_one(mi, 3, af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Stage s lives in ring slot s % 4 and LDS buffer s % 4.  Stages are
@@ -294,11 +333,8 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
                     const v8i a_nx = read_a(mi < 3 ? b0 : b0 + 1, mi < 3 ? mi + 1 : 0);
-                    mfma_row(mi, a_cur, bfr[0]);
                     TFQ_FENCE();
-                    lstore_j(b2, ga[b2], gb[b2], mi);
-                    gload_j(kt + b0 + 6, ga[b2], gb[b2], mi);
-                    TFQ_FENCE();
+                    row_interleaved(mi, a_cur, bfr[0], b2, ga[b2], gb[b2], kt + b0 + 6, mi);
                     a_cur = a_nx;
                 }
                 a0[1] = a_cur;
@@ -309,18 +345,13 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
                 for (int mi = 0; mi < 3; ++mi) {
                     const v8i a_nx = read_a(b0 + 1, mi + 1);
-                    mfma_row(mi, a_cur, bfr[1]);
                     TFQ_FENCE();
                     if (mi == 0) {
                         lstore_j(b3, ga[b3], gb[b3], 0);
                         gload_j(kt + b0 + 7, ga[b3], gb[b3], 0);
-                        lstore_j(b3, ga[b3], gb[b3], 1);
-                        gload_j(kt + b0 + 7, ga[b3], gb[b3], 1);
-                    } else {
-                        lstore_j(b3, ga[b3], gb[b3], mi + 1);
-                        gload_j(kt + b0 + 7, ga[b3], gb[b3], mi + 1);
+                        TFQ_FENCE();
                     }
-                    TFQ_FENCE();
+                    row_interleaved(mi, a_cur, bfr[1], b3, ga[b3], gb[b3], kt + b0 + 7, mi + 1);
                     a_cur = a_nx;
                 }
                 lds_barrier();
