@@ -114,12 +114,12 @@ __device__ __forceinline__ float gelu_tanh(float h)
 // 2 LDS buffers, one barrier per stage; 4 waves x (128 x 128) with
 // v_mfma_f32_32x32x64_f8f6f4 (FP8) or 2x v_mfma_i32_32x32x32_i8 (INT8).
 // ---------------------------------------------------------------------------
-constexpr int PK = 64;                // K bytes per stage
+constexpr int PK = 128;               // K bytes per stage: whole 128-byte lines
 constexpr int PD = 4;                 // register stages in the ring
-constexpr int PA = BM * PK;           // 16 KB of A per stage
-constexpr int PSTAGE = PA + BN * PK;  // 32 KB per LDS buffer
+constexpr int PA = BM * PK;           // 32 KB of A per stage
+constexpr int PSTAGE = PA + BN * PK;  // 64 KB per LDS buffer
 constexpr int EPITCH = 272;           // bytes per staged output row (256 + 16)
-constexpr int PBUF = 4;               // LDS buffers (one barrier per two stages)
+constexpr int PBUF = 2;               // LDS buffers: stages in flight
 constexpr int PSMEM = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -129,6 +129,25 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer resource of `records` bytes from `base` (raw, no swizzle, loads
+// past the end return zero): word 3 is the gfx950 data-format word of an
+// untyped 32-bit buffer.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, int records)
+{
+    const uint64_t a = (uint64_t)base;
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), records, 0x00020000};
+}
+
+// 64 lanes x 16 bytes from the buffer at per-lane byte offset `off` straight
+// into LDS [lds, lds + 1024), lane l at lds + 16 l.  The compiler does not see
+// this load: the caller orders it with explicit vmcnt waits.
+__device__ __forceinline__ void lds_dma16(const v4i& rsrc, int off, uint32_t lds)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
 }
 
 template <int QT>
@@ -155,30 +174,37 @@ void gemm_pipe_kernel(const Params p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.k;
     const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+    const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
+    const v4i rb = buffer_rsrc(p.b + (int64_t)n0 * K, rows_b * K);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-    // global -> registers: chunk (t & 3) of rows (t >> 2) + 64 j, j = 0..3, of A and B
-    const int lc = t & 3, lr = t >> 2;
-    const int voff = lr * K + lc * 16;
-    const int stride64 = 64 * K;
-    // registers -> LDS: 64-byte rows, 16-byte chunk index XOR ((row >> 2) & 3).
-    // The LDS serves a ds_read_b128 16 lanes per cycle from 64 banks; the 16
-    // lanes read 16 consecutive rows at one logical chunk, and this swizzle
-    // puts them in 16 different 16-byte bank groups (the writes, 4 rows x 4
-    // chunks per 16 lanes, are conflict-free too).
-    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
-    // LDS -> fragments: lane reads row (lane & 31), bytes [32 h, 32 h + 32)
-    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
-    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
-    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
+    // LDS rows are 128 bytes (one stage of K); the 16-byte chunk index is
+    // XOR-swizzled with (row >> 1) & 7.  The LDS serves a ds_read_b128 16
+    // lanes per cycle from 64 banks; the 16 lanes of a fragment read take 16
+    // consecutive rows at one logical chunk, and with the swizzle row parity
+    // and physical chunk together name 16 different 16-byte bank groups.
+    //
+    // global -> LDS: each wave moves 8-row groups 8 w + j (j = 0..7) of A
+    // and of B with one 1 KB LDS-DMA load each; every row of a group is one
+    // whole 128-byte line of the operand.  Lane l lands at byte 16 l of the
+    // group -- row l >> 3, physical chunk l & 7 -- so it fetches logical
+    // chunk (l & 7) ^ ((row >> 1) & 7), which is (l & 7) ^ (l >> 4) in even
+    // groups and that ^ 4 in odd ones.
+    const int lc_e = (lane & 7) ^ (lane >> 4), lc_o = lc_e ^ 4;
+    const int row_off = (64 * wave + (lane >> 3)) * K;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+    // LDS -> fragments: for K step ks (0, 1) of a stage, lane reads row
+    // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1
+    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 1) & 7;
+    int rd[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) rd[ks][e] = fr * PK + (((4 * ks + 2 * h + e) ^ sw) << 4);
     const int a_rd = wm * 128 * PK;
     const int b_rd = PA + wn * 128 * PK;
     const int KT = (K + PK - 1) / PK;
 
-    v4u ga[PD][4], gb[PD][4];
     typedef typename PipeAcc<QT>::type acc_t;
     acc_t acc[4][4];
 #pragma unroll
@@ -188,180 +214,104 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    // Loads past the end of K (the K tail and the padding stages up to a
-    // multiple of 4) get bit 31 set in their offset: out of range, they read
-    // zeros.  Keeping this branch-free lets the compiler count the loads in
-    // flight exactly.
-    auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[4]) {
+    // Load of group j (0..7) of A (ab = 0) or B (ab = 1) of stage kt into
+    // LDS buffer kt & 1.  Loads past the end of K (the K tail and the
+    // padding stages up to an even count) get bit 31 set in their offset:
+    // out of range, they write zeros.
+    auto dma = [&](int kt, int ab, int j) {
         const int k0 = kt * PK;
-        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+        const int lc = (j & 1) ? lc_o : lc_e;
+        const int off = (row_off + j * 8 * K + k0 + lc * 16) |
+                        (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+        const uint32_t dst = lds_base + (uint32_t)((kt & 1) * PSTAGE + ab * PA + (8 * wave_u + j) * 1024);
+        lds_dma16(ab ? rb : ra, off, dst);
+    };
+    // fragments of one K step: B of the 4 column tiles, A of the 4 row tiles
+    struct Frags {
+        v8i b[4], a[4];
+    };
+    // half e of fragment q (B tiles 0..3, then A tiles 0..3) of K step ks
+    auto read_part = [&](int buf, int ks, Frags& f, int q, int e) {
+        const uint8_t* s = smem + buf * PSTAGE + (q < 4 ? b_rd + q * 32 * PK : a_rd + (q - 4) * 32 * PK);
+        const v4i v = *reinterpret_cast<const v4i*>(s + rd[ks][e]);
+        v8i& d = q < 4 ? f.b[q] : f.a[q - 4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int off = (voff + j * stride64 + k0) | oob;
-            da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-            db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
     };
-    auto lstore = [&](int buf, const v4u (&da)[4], const v4u (&db)[4]) {
-        uint8_t* s = smem + buf * PSTAGE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
-            *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
-        }
-    };
-    // fragment reads: B fragments of all 4 column tiles, A fragment of row tile mi
-    auto read_b = [&](int buf, v8i (&bf)[4]) {
-        const uint8_t* s = smem + buf * PSTAGE;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const v4i lo = *reinterpret_cast<const v4i*>(s + b_rd + ni * 32 * PK + rd0);
-            const v4i hi = *reinterpret_cast<const v4i*>(s + b_rd + ni * 32 * PK + rd1);
-            bf[ni] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-    };
-    auto read_a = [&](int buf, int mi) -> v8i {
-        const uint8_t* s = smem + buf * PSTAGE;
-        const v4i lo = *reinterpret_cast<const v4i*>(s + a_rd + mi * 32 * PK + rd0);
-        const v4i hi = *reinterpret_cast<const v4i*>(s + a_rd + mi * 32 * PK + rd1);
-        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto mfma_one = [&](int mi, int ni, const v8i& af, const v8i (&bf)[4]) {
+    // weights as the first operand: the 32x32 result is the transposed
+    // output tile, so each lane ends up with 4 consecutive columns
+    auto mfma_one = [&](int mi, int ni, const Frags& f) {
         if constexpr (QT == kE4M3FN) {
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[ni], af, acc[mi][ni], 0, 0, 0, 0, 0, 0);
+                f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, 0, 0, 0);
         } else {
-            const v8i b8 = bf[ni];
+            const v8i b8 = f.b[ni], a8 = f.a[mi];
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{af[0], af[1], af[2], af[3]}, acc[mi][ni],
+                v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{a8[0], a8[1], a8[2], a8[3]}, acc[mi][ni],
                 0, 0, 0);
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{af[4], af[5], af[6], af[7]}, acc[mi][ni],
+                v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{a8[4], a8[5], a8[6], a8[7]}, acc[mi][ni],
                 0, 0, 0);
         }
     };
-    auto mfma_row = [&](int mi, const v8i& af, const v8i (&bf)[4]) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            // weights as the first operand: the 32x32 result is the transposed
-            // output tile, so each lane ends up with 4 consecutive columns
-            if constexpr (QT == kE4M3FN) {
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bf[ni], af, acc[mi][ni], 0, 0, 0, 0, 0, 0);
-            } else {
-                const v8i b8 = bf[ni];
-                acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    v4i{b8[0], b8[1], b8[2], b8[3]}, v4i{af[0], af[1], af[2], af[3]}, acc[mi][ni],
-                    0, 0, 0);
-                acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{af[4], af[5], af[6], af[7]}, acc[mi][ni],
-                    0, 0, 0);
-            }
-        }
-    };
-
-    // one 16-byte chunk (A and B) of a ring slot: load, or write to LDS
-    auto gload_j = [&](int kt, v4u (&da)[4], v4u (&db)[4], int j) {
-        const int k0 = kt * PK;
-        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
-        const int off = (voff + j * stride64 + k0) | oob;
-        da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-        db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-    };
-    auto lstore_j = [&](int buf, const v4u (&da)[4], const v4u (&db)[4], int j) {
-        uint8_t* s = smem + buf * PSTAGE;
-        *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
-        *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
-    };
-    // one MFMA row with one memory operation after each MFMA:
-    // write A chunk j, write B chunk j, load A chunk j, load B chunk j
-    auto row_interleaved = [&](int mi, const v8i& af, const v8i (&bf)[4], int buf, v4u (&da)[4],
-                               v4u (&db)[4], int kt_load, int j) {
-        uint8_t* s = smem + buf * PSTAGE;
-        const int k0 = kt_load * PK;
-        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
-        const int off = (voff + j * stride64 + k0) | oob;
-        mfma_one(mi, 0, af, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_one(mi, 1, af, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_one(mi, 2, af, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_one(mi, 3, af, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Stage s lives in ring slot s % 4 and LDS buffer s % 4.  Stages are
-    // processed in pairs with one barrier per pair: while pair (s, s+1) is
-    // computed, stages s+2 and s+3 move from their ring slots into the LDS
-    // buffers of s-2 and s-1 (free since the previous barrier) and the slots
-    // are refilled with stages s+6 and s+7 -- loads are issued 4 stages ahead.
-    // The barrier sits before the last row tile of stage s+1; stage s+2's
-    // first fragments are read while that row's MFMAs run.  Scheduling
-    // fences keep one chunk of LDS writes and loads between consecutive
-    // MFMA rows.  The loop runs a multiple of 4 stages (stages past K read
-    // zeros).
-    v8i bfr[2][4];
-    v8i a0[2];
-#pragma unroll
-    for (int u = 0; u < PD; ++u) gload(u, ga[u], gb[u]);
-    lstore(0, ga[0], gb[0]);
-    lstore(1, ga[1], gb[1]);
-    gload(4, ga[0], gb[0]);
-    gload(5, ga[1], gb[1]);
-    lds_barrier();
-    read_b(0, bfr[0]);
-    a0[0] = read_a(0, 0);
-
 #define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
-    for (int kt = 0; kt < KT; kt += PD) {
+
+    // Stage s (128 bytes of K) lives in LDS buffer s & 1 and is computed as
+    // two K steps of 16 MFMAs.  One barrier per stage, between its K steps:
+    // by then every wave has read all of stage s's fragments (the second K
+    // step's were read during the first) and has received its own loads of
+    // stage s + 1, so buffer s & 1 is free and stage s + 1 complete.  The
+    // second K step then reads stage s + 1's first fragments, one 16-byte
+    // read after each MFMA, and issues the 16 loads of stage s + 2 into the
+    // freed buffer, two after each of its first 8 MFMAs.  The loop runs an
+    // even number of stages (a stage past K reads zeros).
+    Frags f0, f1;
 #pragma unroll
-        for (int P = 0; P < 2; ++P) {
-            const int b0 = 2 * P, b2 = (b0 + 2) & 3, b3 = (b0 + 3) & 3;
-            // first stage of the pair: buffer b0, fragments in set 0
-            {
-                read_b(b0 + 1, bfr[1]);
-                v8i a_cur = a0[0];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    const v8i a_nx = read_a(mi < 3 ? b0 : b0 + 1, mi < 3 ? mi + 1 : 0);
-                    TFQ_FENCE();
-                    row_interleaved(mi, a_cur, bfr[0], b2, ga[b2], gb[b2], kt + b0 + 6, mi);
-                    a_cur = a_nx;
-                }
-                a0[1] = a_cur;
+        for (int j = 0; j < 8; ++j) {
+            dma(u, 0, j);
+            dma(u, 1, j);
+        }
+    // stage 0 complete: the 16 loads of stage 1 may still be in flight
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        read_part(0, 0, f0, q, 0);
+        read_part(0, 0, f0, q, 1);
+    }
+
+    for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            // K step 0 of stage kt+u from f0; K step 1's fragments into f1
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mfma_one(i >> 2, i & 3, f0);
+                TFQ_FENCE();
+                read_part(u, 1, f1, i >> 1, i & 1);
+                TFQ_FENCE();
             }
-            // second stage: buffer b0 + 1, fragments in set 1
-            {
-                v8i a_cur = a0[1];
+            // own loads of stage kt+u+1 (the only ones in flight) are done
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // K step 1 from f1; stage kt+u+1's first fragments into f0 and
+            // the loads of stage kt+u+2
 #pragma unroll
-                for (int mi = 0; mi < 3; ++mi) {
-                    const v8i a_nx = read_a(b0 + 1, mi + 1);
-                    TFQ_FENCE();
-                    if (mi == 0) {
-                        lstore_j(b3, ga[b3], gb[b3], 0);
-                        gload_j(kt + b0 + 7, ga[b3], gb[b3], 0);
-                        TFQ_FENCE();
-                    }
-                    row_interleaved(mi, a_cur, bfr[1], b3, ga[b3], gb[b3], kt + b0 + 7, mi + 1);
-                    a_cur = a_nx;
+            for (int i = 0; i < 16; ++i) {
+                mfma_one(i >> 2, i & 3, f1);
+                TFQ_FENCE();
+                read_part(u ^ 1, 0, f0, i >> 1, i & 1);
+                if (i < 8) {
+                    dma(kt + u + 2, 0, i);
+                    dma(kt + u + 2, 1, i);
                 }
-                lds_barrier();
-                read_b(b2, bfr[0]);
-                a0[0] = read_a(b2, 0);
-                mfma_row(3, a_cur, bfr[1]);
+                TFQ_FENCE();
             }
         }
     }
 #undef TFQ_FENCE
+    // the loads of the padding stages past the loop are still in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue ----
     // With the weights as the first MFMA operand, lane (fr, h) holds, for row
@@ -452,8 +402,10 @@ void gemm_pipe_kernel(const Params p)
 // acc += temp * (s_a[row, kb] * s_b[nb, kb]).  Same register-staged pipeline
 // as gemm_pipe_kernel with a 2-stage ring.
 // ---------------------------------------------------------------------------
+constexpr int QK = 64;                     // K bytes per stage
+constexpr int QA = BM * QK;                // 16 KB of A per stage
 constexpr int QBN = 128;                   // output columns per workgroup
-constexpr int QSTAGE = PA + QBN * PK;      // 24 KB per LDS buffer
+constexpr int QSTAGE = QA + QBN * QK;      // 24 KB per LDS buffer
 constexpr int QEPITCH = 144;               // staged output row: 64 columns * 2 B + 16
 constexpr int QSMEM = (2 * QSTAGE > 4 * 128 * QEPITCH) ? 2 * QSTAGE : 4 * 128 * QEPITCH;
 constexpr int QD = 2;                      // register stages in the block kernel's ring
@@ -483,13 +435,13 @@ void gemm_block_kernel(const Params p)
     const int lc = t & 3, lr = t >> 2;
     const int voff = lr * K + lc * 16;
     const int stride64 = 64 * K;
-    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
+    const int lds_w = lr * QK + ((lc ^ ((lr >> 2) & 3)) << 4);
     const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
-    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
-    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
-    const int a_rd = wm * 128 * PK;
-    const int b_rd = PA + wn * 64 * PK;
-    const int KT = K / PK;  // even: K % 128 == 0
+    const int rd0 = fr * QK + (((2 * h) ^ sw) << 4);
+    const int rd1 = fr * QK + (((2 * h + 1) ^ sw) << 4);
+    const int a_rd = wm * 128 * QK;
+    const int b_rd = QA + wn * 64 * QK;
+    const int KT = K / QK;  // even: K % 128 == 0
 
     v4u ga[QD][4], gb[QD][2];
     v16f acc[4][2], tmp[4][2];
@@ -501,7 +453,7 @@ void gemm_block_kernel(const Params p)
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[2]) {
-        const int k0 = kt * PK;
+        const int k0 = kt * QK;
         const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -514,8 +466,8 @@ void gemm_block_kernel(const Params p)
         uint8_t* s = smem + buf * QSTAGE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
-            if (j < 2) *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * QK) = da[j];
+            if (j < 2) *reinterpret_cast<v4u*>(s + QA + lds_w + j * 64 * QK) = db[j];
         }
     };
     auto frag = [&](const uint8_t* s) -> v8i {
@@ -541,10 +493,10 @@ void gemm_block_kernel(const Params p)
         const uint8_t* s = smem + buf * QSTAGE;
         v8i bf[2];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * PK);
+        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * QK);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const v8i af = frag(s + a_rd + mi * 32 * PK);
+            const v8i af = frag(s + a_rd + mi * 32 * QK);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
                 tmp[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -648,13 +600,13 @@ void gemm_dual_kernel(const Params p)
     const int lc = t & 3, lr = t >> 2;
     const int voff = lr * K + lc * 16;
     const int stride64 = 64 * K;
-    const int lds_w = lr * PK + ((lc ^ ((lr >> 2) & 3)) << 4);
+    const int lds_w = lr * QK + ((lc ^ ((lr >> 2) & 3)) << 4);
     const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
-    const int rd0 = fr * PK + (((2 * h) ^ sw) << 4);
-    const int rd1 = fr * PK + (((2 * h + 1) ^ sw) << 4);
-    const int a_rd = wm * 128 * PK;
-    const int b_rd = PA + wn * 64 * PK;
-    const int KT = (K + PK - 1) / PK;
+    const int rd0 = fr * QK + (((2 * h) ^ sw) << 4);
+    const int rd1 = fr * QK + (((2 * h + 1) ^ sw) << 4);
+    const int a_rd = wm * 128 * QK;
+    const int b_rd = QA + wn * 64 * QK;
+    const int KT = (K + QK - 1) / QK;
 
     typedef typename PipeAcc<QT>::type acc_t;
     v4u ga[3][4], gb[3][2];
@@ -667,7 +619,7 @@ void gemm_dual_kernel(const Params p)
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
     auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[2]) {
-        const int k0 = kt * PK;
+        const int k0 = kt * QK;
         const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -680,8 +632,8 @@ void gemm_dual_kernel(const Params p)
         uint8_t* s = smem + buf * QSTAGE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * PK) = da[j];
-            if (j < 2) *reinterpret_cast<v4u*>(s + PA + lds_w + j * 64 * PK) = db[j];
+            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * QK) = da[j];
+            if (j < 2) *reinterpret_cast<v4u*>(s + QA + lds_w + j * 64 * QK) = db[j];
         }
     };
     auto frag = [&](const uint8_t* s) -> v8i {
@@ -693,10 +645,10 @@ void gemm_dual_kernel(const Params p)
         const uint8_t* s = smem + buf * QSTAGE;
         v8i bf[2];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * PK);
+        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * QK);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const v8i af = frag(s + a_rd + mi * 32 * PK);
+            const v8i af = frag(s + a_rd + mi * 32 * QK);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) {
                 if constexpr (QT == kE4M3FN) {
