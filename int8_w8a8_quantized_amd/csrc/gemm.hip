@@ -81,6 +81,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return __builtin_bit_cast(uint16_t, __float2bfloat16(f));
 }
 
+// two floats -> two BF16 (RNE) in one 32-bit word, lo in the low half: one
+// v_cvt_pk_bf16_f32
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
+}
+
 // (v * s_row) * s_col and + bias, each rounded on its own (never fused into
 // an FMA): the fixed order that makes the INT8 BF16 output reproducible.
 __device__ __forceinline__ float scale_out(float v, float srow, float scol)
@@ -120,7 +129,10 @@ constexpr int PA = BM * PK;           // 32 KB of A per stage
 constexpr int PSTAGE = PA + BN * PK;  // 64 KB per LDS buffer
 constexpr int EPITCH = 272;           // bytes per staged output row (256 + 16)
 constexpr int PBUF = 2;               // LDS buffers: stages in flight
-constexpr int PSMEM = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
+// the tile's row scales, column scales and BF16 bias (1 KB each) sit past
+// both the pipeline buffers and the output staging area
+constexpr int PSCL = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
+constexpr int PSMEM = PSCL + 3 * 1024;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -136,8 +148,12 @@ __device__ __forceinline__ void lds_barrier()
 // untyped 32-bit buffer.
 __device__ __forceinline__ v4i buffer_rsrc(const void* base, int records)
 {
+    // readfirstlane: the inline-asm loads need the descriptor in SGPRs even
+    // where the compiler cannot prove the value uniform
     const uint64_t a = (uint64_t)base;
-    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), records, 0x00020000};
+    return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane(records), 0x00020000};
 }
 
 // 64 lanes x 16 bytes from the buffer at per-lane byte offset `off` straight
@@ -266,6 +282,15 @@ void gemm_pipe_kernel(const Params p)
     // freed buffer, two after each of its first 8 MFMAs.  The loop runs an
     // even number of stages (a stage past K reads zeros).
     Frags f0, f1;
+    // waves 0, 1, 2 fetch the tile's row scales, column scales and bias into
+    // LDS (past the end: zeros); issued first, so the prologue's wait covers them
+    if (wave_u == 0) {
+        lds_dma16(buffer_rsrc(p.sa + m0, rows_a * 4), lane * 16, lds_base + PSCL);
+    } else if (wave_u == 1) {
+        lds_dma16(buffer_rsrc(p.sb + n0, rows_b * 4), lane * 16, lds_base + PSCL + 1024);
+    } else if (wave_u == 2 && p.bias != nullptr) {
+        lds_dma16(buffer_rsrc(p.bias + n0, rows_b * 2), lane * 16, lds_base + PSCL + 2048);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -318,12 +343,12 @@ void gemm_pipe_kernel(const Params p)
     // tile mi and column tile ni, output row  wm*128 + mi*32 + fr  and the
     // four consecutive output columns  wn*128 + ni*32 + 8q + 4h + (0..3)  in
     // registers 4q..4q+3 (q = 0..3).
+    const float* lds_sa = reinterpret_cast<const float*>(smem + PSCL);
+    const float* lds_sb = reinterpret_cast<const float*>(smem + PSCL + 1024);
+    const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + PSCL + 2048);
     float srow[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int row = m0 + wm * 128 + mi * 32 + fr;
-        srow[mi] = row < p.m ? p.sa[row] : 0.0f;
-    }
+    for (int mi = 0; mi < 4; ++mi) srow[mi] = lds_sa[wm * 128 + mi * 32 + fr];
     if constexpr (WANT_ACC) {
         // raw INT32 sums: 16-byte stores of 4 consecutive columns
 #pragma unroll
@@ -348,34 +373,44 @@ void gemm_pipe_kernel(const Params p)
         // with 16-byte stores.
         lds_barrier();  // every wave is done with the pipeline buffers
         uint8_t* stg = smem + wave * 128 * EPITCH;
+        // one branch-free pass per bias case
+        auto stage = [&](auto has_bias) {
+            constexpr bool HB = decltype(has_bias)::value;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+            for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c0 = n0 + wn * 128 + ni * 32 + 8 * q + 4 * h;
-                float sc[4], bc[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = c0 + j < p.n;
-                    sc[j] = ok ? p.sb[c0 + j] : 0.0f;
-                    bc[j] = (p.bias != nullptr && ok) ? bf16_to_f32(p.bias[c0 + j]) : 0.0f;
-                }
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    float v[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[j]);
-                        if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
-                        if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                for (int q = 0; q < 4; ++q) {
+                    const int lc0 = wn * 128 + ni * 32 + 8 * q + 4 * h;
+                    const v4f sc = *reinterpret_cast<const v4f*>(lds_sb + lc0);
+                    float bc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (HB) {
+                        const uint2 b2 = *reinterpret_cast<const uint2*>(lds_bias + lc0);
+                        bc[0] = __uint_as_float(b2.x << 16);
+                        bc[1] = __uint_as_float(b2.x & 0xffff0000u);
+                        bc[2] = __uint_as_float(b2.y << 16);
+                        bc[3] = __uint_as_float(b2.y & 0xffff0000u);
                     }
-                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH +
-                                              (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        float v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[j]);
+                            if constexpr (HB) v[j] = add_bias(v[j], bc[j]);
+                            if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                        }
+                        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+                        const uint32_t hi = pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH +
+                                                  (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+                    }
                 }
             }
-        }
+        };
+        if (p.bias != nullptr)
+            stage(std::true_type{});
+        else
+            stage(std::false_type{});
         // the wave reads back only what it wrote itself
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int ch = lane & 15;
@@ -551,8 +586,8 @@ void gemm_block_kernel(const Params p)
                     if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
                     if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
                 }
-                const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                const uint32_t lo = pack_bf16x2(v[0], v[1]);
+                const uint32_t hi = pack_bf16x2(v[2], v[3]);
                 *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH +
                                           (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
             }
@@ -739,8 +774,8 @@ void gemm_dual_kernel(const Params p)
                         if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
                         if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
                     }
-                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const uint32_t lo = pack_bf16x2(v[0], v[1]);
+                    const uint32_t hi = pack_bf16x2(v[2], v[3]);
                     *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH +
                                               (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
                 }
