@@ -11,11 +11,14 @@
 //  * both operands are K-contiguous ("TN"), the layout MFMA operands want;
 //  * the K order inside an MFMA does not change the sum as long as A and B
 //    use the same one, so each lane group reads 32 contiguous bytes;
-//  * global -> registers through 128-bit buffer loads (out-of-range rows and
-//    the K tail read as zero, so ragged M/N/K need no branches), a ring of
-//    register stages keeps several K stages of loads in flight while MFMAs
-//    run, then registers -> LDS (64-byte rows, chunk swizzled to be free of
-//    bank conflicts) -> MFMA fragments;
+//  * main kernel: operands go from global memory straight into LDS with
+//    buffer loads carrying the LDS modifier (no VGPR staging, no LDS write
+//    instructions), in 128-byte K stages so that every row load is one whole
+//    cache line; out-of-range rows and the K tail read as zero, so ragged
+//    M/N/K need no branches; LDS rows are chunk-swizzled to be free of bank
+//    conflicts for the MFMA fragment reads;
+//  * the block-scaled and two-workgroups-per-CU kernels stage 64-byte K
+//    stages through a ring of VGPRs (128-bit buffer loads) into LDS;
 //  * the weights are the first MFMA operand, so each lane finishes with four
 //    consecutive output columns of one row; the epilogue scales in FP32,
 //    stages BF16 rows in LDS and writes whole row segments with 16-byte
@@ -117,14 +120,13 @@ __device__ __forceinline__ float gelu_tanh(float h)
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel for per-token / per-channel scales.  64 K-bytes per stage;
-// a ring of 4 register stages of 128-bit buffer loads keeps 3 stages of
-// global loads in flight (the compiler tracks them with exact vmcnt waits),
-// 2 LDS buffers, one barrier per stage; 4 waves x (128 x 128) with
-// v_mfma_f32_32x32x64_f8f6f4 (FP8) or 2x v_mfma_i32_32x32x32_i8 (INT8).
+// Main kernel for per-token / per-channel scales: 256x256 output tile, 4
+// waves x (128 x 128) with v_mfma_f32_32x32x64_f8f6f4 (FP8) or 2x
+// v_mfma_i32_32x32x32_i8 (INT8), accumulators in AGPRs (one wave per SIMD).
+// 128 K-bytes per stage, 2 LDS buffers of 64 KB filled by LDS-DMA loads one
+// stage ahead, one barrier per stage.
 // ---------------------------------------------------------------------------
 constexpr int PK = 128;               // K bytes per stage: whole 128-byte lines
-constexpr int PD = 4;                 // register stages in the ring
 constexpr int PA = BM * PK;           // 32 KB of A per stage
 constexpr int PSTAGE = PA + BN * PK;  // 64 KB per LDS buffer
 constexpr int EPITCH = 272;           // bytes per staged output row (256 + 16)
