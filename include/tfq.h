@@ -126,7 +126,8 @@ tfq_status tfq_quantize_weight_per_channel(const void* w_bf16, int64_t n, int64_
  *   channel per row): both K-contiguous, 16-byte aligned.
  *   scale_block 0:   a_scale [m], b_scale [n].
  *   scale_block 128: a_scale [m, k/128] (1x128 groups), b_scale [n/128, k/128]
- *                    (128x128 blocks); k % 128 == 0, n % 128 == 0.
+ *                    (128x128 blocks); k % 128 == 0, n % 128 == 0,
+ *                    k <= 131072 (else TFQ_ERR_BAD_SHAPE).
  *   bias_bf16  [n] BF16 or NULL, added after scaling (before GELU).
  *   epi        tfq_epilogue.
  *   y_bf16     [m, n] BF16, 16-byte aligned.

@@ -114,7 +114,8 @@ tfq_status validate_gemm(const void* a, const float* sa, const void* b, const fl
     if (m < 1 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 || k < 16 || k > kmax ||
         k % 16 != 0)
         return TFQ_ERR_BAD_SHAPE;
-    if (block == 128 && (k % 128 != 0 || n % 128 != 0)) return TFQ_ERR_BAD_SHAPE;
+    // block mode keeps one row of weight-block scales (k/128 floats) in 4 KB of LDS
+    if (block == 128 && (k % 128 != 0 || n % 128 != 0 || k > 131072)) return TFQ_ERR_BAD_SHAPE;
     const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
     if (tiles > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||

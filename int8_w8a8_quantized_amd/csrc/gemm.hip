@@ -168,6 +168,16 @@ __device__ __forceinline__ void lds_dma16(const v4i& rsrc, int off, uint32_t lds
                  : "memory");
 }
 
+// Lane id (0..63) computed in place by an asm block the compiler cannot hoist
+// or merge: values derived from it are rebuilt where they are used instead of
+// being kept live (and spilled) across long loops.
+__device__ __forceinline__ int lane_id_here()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 template <int QT>
 struct PipeAcc;
 template <>
@@ -434,53 +444,107 @@ void gemm_pipe_kernel(const Params p)
 // output tile, 4 waves (2x2) of 128x64, so every wave's 64 columns lie in one
 // 128-wide weight block and -- with the weights as the first MFMA operand --
 // every lane's output row is fixed per 32-row tile: the scale of a
-// (row, K-block) pair is one float per row tile.  Each 128-deep K block is
-// two 64-deep stages whose MFMAs accumulate into a temporary; then
-// acc += temp * (s_a[row, kb] * s_b[nb, kb]).  Same register-staged pipeline
-// as gemm_pipe_kernel with a 2-stage ring.
+// (row, K-block) pair is one float per row tile.  One stage is one 128-deep
+// K block (two K steps of MFMAs into a temporary); the next block's first K
+// step folds it in, acc += temp * (s_a[row, kb] * s_b[nb, kb]), one tile
+// before each of its MFMAs.  Operands go straight into LDS (LDS-DMA loads,
+// whole 128-byte lines), 3 LDS buffers, loads 3 stages ahead, one barrier
+// per stage; the row scales of each block come with the stage (4-byte
+// LDS-DMA loads), the weight block's scale by a scalar load.
 // ---------------------------------------------------------------------------
 constexpr int QK = 64;                     // K bytes per stage
 constexpr int QA = BM * QK;                // 16 KB of A per stage
 constexpr int QBN = 128;                   // output columns per workgroup
 constexpr int QSTAGE = QA + QBN * QK;      // 24 KB per LDS buffer
 constexpr int QEPITCH = 144;               // staged output row: 64 columns * 2 B + 16
-constexpr int QSMEM = (2 * QSTAGE > 4 * 128 * QEPITCH) ? 2 * QSTAGE : 4 * 128 * QEPITCH;
-constexpr int QD = 2;                      // register stages in the block kernel's ring
 constexpr int DSMEM = (3 * QSTAGE > 4 * 128 * QEPITCH) ? 3 * QSTAGE : 4 * 128 * QEPITCH;
+constexpr int XB_A = BM * 128;                 // 32 KB of A per stage
+constexpr int XB_STAGE = XB_A + QBN * 128;      // 48 KB per LDS buffer
+constexpr int XB_BUF = 3;
+constexpr int XB_SA = XB_BUF * XB_STAGE;        // row-scale ring: 3 x 1 KB
+constexpr int XB_BIAS = XB_SA + XB_BUF * 1024;  // the tile's 128 BF16 bias values
+constexpr int XB_SB = XB_BIAS + 256;            // the weight block's scales, K/128 <= 1024
+constexpr int XB_SMEM = XB_SB + 4096;
+
+// 64 lanes x 4 bytes from the buffer at per-lane byte offset `off` straight
+// into LDS [lds, lds + 256), lane l at lds + 4 l (caller orders with vmcnt)
+__device__ __forceinline__ void lds_dma4(const v4i& rsrc, int off, uint32_t lds)
+{
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
 
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_block_kernel(const Params p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[QSMEM];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[XB_SMEM];
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wave_u = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int wm = wave_u & 1, wn = wave_u >> 1;
+    const int lane = lane_id_here();
     int tm, tn;
     map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * QBN;
     const int K = p.k;
-    const int kblocks = K >> 7;
+    const int KT = K >> 7;  // K blocks = stages (K % 128 == 0)
     const int rows_a = min(BM, p.m - m0), rows_b = min(QBN, p.n - n0);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+    const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
+    const v4i rb = buffer_rsrc(p.b + (int64_t)n0 * K, rows_b * K);
+    const v4i rsa = buffer_rsrc(p.sa + (int64_t)m0 * KT, rows_a * KT * 4);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-    // global -> registers: chunk (t & 3) of A rows (t >> 2) + 64 j (j < 4) and
-    // of B rows (t >> 2) + 64 j (j < 2)
-    const int lc = t & 3, lr = t >> 2;
-    const int voff = lr * K + lc * 16;
-    const int stride64 = 64 * K;
-    const int lds_w = lr * QK + ((lc ^ ((lr >> 2) & 3)) << 4);
-    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 2) & 3;
-    const int rd0 = fr * QK + (((2 * h) ^ sw) << 4);
-    const int rd1 = fr * QK + (((2 * h + 1) ^ sw) << 4);
-    const int a_rd = wm * 128 * QK;
-    const int b_rd = QA + wn * 64 * QK;
-    const int KT = K / QK;  // even: K % 128 == 0
+    // global -> LDS: wave w moves 8-row groups 8 w + j (j < 8) of A and
+    // 4 w + j (j < 4) of B per stage, one 1 KB LDS-DMA load each; lane l
+    // lands at row l >> 3, physical chunk l & 7 of its group and fetches
+    // logical chunk (l & 7) ^ ((row >> 1) & 7) (the LDS swizzle for 128-byte
+    // rows), which is (l & 7) ^ (l >> 4) in even groups and that ^ 4 in odd.
+    const int lc_e = (lane & 7) ^ (lane >> 4), lc_o = lc_e ^ 4;
+    const int a_off = (64 * wave_u + (lane >> 3)) * K;
+    const int b_off = (32 * wave_u + (lane >> 3)) * K;
+    // the row scales of block kb: wave w fetches rows 64 w + lane
+    const int sa_off = (64 * wave_u + lane) * KT * 4;
+    auto dma_stage = [&](int kt, int buf) {
+        const int k0 = kt * 128;
+        const int oob_e = (int)((unsigned)(k0 + lc_e * 16 >= K) << 31);
+        const int oob_o = (int)((unsigned)(k0 + lc_o * 16 >= K) << 31);
+        const uint32_t dst = lds_base + (uint32_t)(buf * XB_STAGE);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int lc = (j & 1) ? lc_o : lc_e, oob = (j & 1) ? oob_o : oob_e;
+            lds_dma16(ra, (a_off + j * 8 * K + k0 + lc * 16) | oob, dst + (8 * wave_u + j) * 1024);
+            if (j < 4)
+                lds_dma16(rb, (b_off + j * 8 * K + k0 + lc * 16) | oob,
+                          dst + XB_A + (4 * wave_u + j) * 1024);
+        }
+        lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
+                 lds_base + XB_SA + buf * 1024 + wave_u * 256);
+    };
+    constexpr int DMA_PER_STAGE = 13;  // per wave: 8 A + 4 B + 1 row-scale load
 
-    v4u ga[QD][4], gb[QD][2];
+    // LDS -> fragments: K step ks (0, 1) of a stage, lane reads row
+    // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1
+    const int fr = lane & 31, h = lane >> 5, sw = (fr >> 1) & 7;
+    int rd[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) rd[ks][e] = fr * 128 + (((4 * ks + 2 * h + e) ^ sw) << 4);
+    const int a_rd = wm * 128 * 128;
+    const int b_rd = XB_A + wn * 64 * 128;
+    struct Frags {
+        v8i b[2], a[4];
+    };
+    // half e of fragment q (B tiles 0, 1, then A tiles 0..3) of K step ks
+    auto read_part = [&](int buf, int ks, Frags& f, int q, int e) {
+        const uint8_t* s = smem + buf * XB_STAGE + (q < 2 ? b_rd + q * 32 * 128 : a_rd + (q - 2) * 32 * 128);
+        const v4i v = *reinterpret_cast<const v4i*>(s + rd[ks][e]);
+        v8i& d = q < 2 ? f.b[q] : f.a[q - 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
+    };
+
     v16f acc[4][2], tmp[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -488,110 +552,135 @@ void gemm_block_kernel(const Params p)
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    float f_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // block scale factors of the previous stage
 
-    auto gload = [&](int kt, v4u (&da)[4], v4u (&db)[2]) {
-        const int k0 = kt * QK;
-        const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+    // prologue: bias and the weight block's scales of every K block (wave
+    // 3; the tile's 128 columns are one weight block), stages 0, 1, 2
+    if (wave_u == 3) {
+        if (p.bias != nullptr) lds_dma4(buffer_rsrc(p.bias + n0, rows_b * 2), lane * 4, lds_base + XB_BIAS);
+        const v4i rsb = buffer_rsrc(p.sb + (int64_t)(n0 >> 7) * KT, KT * 4);
+        for (int c = 0; c < KT; c += 64) lds_dma4(rsb, (c + lane) * 4, lds_base + XB_SB + c * 4);
+    }
+    dma_stage(0, 0);
+    dma_stage(1, 1);
+    dma_stage(2, 2);
+    // bias and stage 0 complete: 26 loads (stages 1, 2) may be in flight
+    asm volatile("s_waitcnt vmcnt(26)\n\ts_barrier" ::: "memory");
+    Frags f0, f1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int off = (voff + j * stride64 + k0) | oob;
-            da[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-            if (j < 2) db[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf, const v4u (&da)[4], const v4u (&db)[2]) {
-        uint8_t* s = smem + buf * QSTAGE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<v4u*>(s + lds_w + j * 64 * QK) = da[j];
-            if (j < 2) *reinterpret_cast<v4u*>(s + QA + lds_w + j * 64 * QK) = db[j];
-        }
-    };
-    auto frag = [&](const uint8_t* s) -> v8i {
-        const v4i lo = *reinterpret_cast<const v4i*>(s + rd0);
-        const v4i hi = *reinterpret_cast<const v4i*>(s + rd1);
-        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    // this lane's output rows (one per 32-row tile) and the K-block scale factors
-    int arow[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = m0 + wm * 128 + mi * 32 + fr;
-    const int nb = (n0 + wn * 64) >> 7;
-    const bool col_ok = n0 + wn * 64 < p.n;
-    auto block_scales = [&](int kb, float (&f)[4]) {
-        const float sb = col_ok ? p.sb[(int64_t)nb * kblocks + kb] : 0.0f;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            f[mi] = (arow[mi] < p.m ? p.sa[(int64_t)arow[mi] * kblocks + kb] : 0.0f) * sb;
-    };
-    // one 64-deep stage of MFMAs into the temporaries (first half of a block
-    // starts them from zero)
-    auto compute = [&](int buf, bool first) {
-        const uint8_t* s = smem + buf * QSTAGE;
-        v8i bf[2];
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) bf[ni] = frag(s + b_rd + ni * 32 * QK);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const v8i af = frag(s + a_rd + mi * 32 * QK);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                tmp[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bf[ni], af, first ? v16f{} : tmp[mi][ni], 0, 0, 0, 0, 0, 0);
-        }
-    };
-
-    gload(0, ga[0], gb[0]);
-    gload(1, ga[1], gb[1]);
-    lstore(0, ga[0], gb[0]);
-    float f[4];
-    // stage s = kt + U: ring slot U, LDS buffer U; U = 0 is the first half of
-    // K block kt/2, U = 1 its second half
-    for (int kt = 0; kt < KT; kt += 2) {
-        lds_barrier();
-        lstore(1, ga[1], gb[1]);
-        gload(kt + 2, ga[0], gb[0]);
-        block_scales(kt >> 1, f);
-        compute(0, true);
-        lds_barrier();
-        lstore(0, ga[0], gb[0]);
-        gload(kt + 3, ga[1], gb[1]);
-        compute(1, false);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[mi][ni][e] = __builtin_fmaf(tmp[mi][ni][e], f[mi], acc[mi][ni][e]);
+    for (int q = 0; q < 6; ++q) {
+        read_part(0, 0, f0, q, 0);
+        read_part(0, 0, f0, q, 1);
     }
 
-    // ---- epilogue: lane holds row arow[mi] and columns
-    // wn*64 + ni*32 + 8q + 4h + (0..3) in registers 4q..4q+3 ----
+    // DMA op d (0..12) of stage kt into buffer bf: A groups, B groups, row scales
+    auto dma_op = [&](int kt, int bf, int d) {
+        const int k0 = kt * 128;
+        const uint32_t dst = lds_base + (uint32_t)(bf * XB_STAGE);
+        if (d < 12) {
+            const int j = d < 8 ? d : d - 8;
+            const int lc = (j & 1) ? lc_o : lc_e;
+            const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+            if (d < 8)
+                lds_dma16(ra, (a_off + j * 8 * K + k0 + lc * 16) | oob, dst + (8 * wave_u + j) * 1024);
+            else
+                lds_dma16(rb, (b_off + j * 8 * K + k0 + lc * 16) | oob,
+                          dst + XB_A + (4 * wave_u + j) * 1024);
+        } else {
+            lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
+                     lds_base + XB_SA + bf * 1024 + wave_u * 256);
+        }
+    };
+    auto mfma = [&](const v16f& c, const Frags& f, int mi, int ni) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], c, 0, 0, 0, 0, 0, 0);
+    };
+
+#define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
+    // Stage kt lives in LDS buffer kt % 3.  Its barrier sits between its two
+    // K steps: by then every wave has read all of its fragments and row
+    // scales and has received its own loads of stage kt + 1 (loads issued
+    // after those: the 13 of stage kt + 2), so the buffer is free for stage
+    // kt + 3, whose loads go out during the second K step together with the
+    // reads of stage kt + 1's first fragments.
+    int buf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int nbuf = buf == XB_BUF - 1 ? 0 : buf + 1;
+        const float sbv = reinterpret_cast<const float*>(smem + XB_SB)[kt];
+        const float* sa_l = reinterpret_cast<const float*>(smem + XB_SA + buf * 1024);
+        float f_cur[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) f_cur[mi] = sa_l[wm * 128 + mi * 32 + fr];
+        // K step 0: fold the previous block's temporary of each tile into acc
+        // just before the tile's first MFMA of this block; K step 1's 12
+        // fragment halves into f1 (1 or 2 after each MFMA)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int mi = i >> 1, ni = i & 1;
+            if (kt > 0) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[mi][ni][e] = __builtin_fmaf(tmp[mi][ni][e], f_prev[mi], acc[mi][ni][e]);
+            }
+            tmp[mi][ni] = mfma(v16f{}, f0, mi, ni);
+            TFQ_FENCE();
+#pragma unroll
+            for (int r = (12 * i) / 8; r < (12 * (i + 1)) / 8; ++r) read_part(buf, 1, f1, r >> 1, r & 1);
+            TFQ_FENCE();
+        }
+        asm volatile("s_waitcnt vmcnt(13)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // K step 1; stage kt+1's K step 0 fragments into f0; stage kt+3's loads
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int mi = i >> 1, ni = i & 1;
+            tmp[mi][ni] = mfma(tmp[mi][ni], f1, mi, ni);
+            TFQ_FENCE();
+#pragma unroll
+            for (int r = (12 * i) / 8; r < (12 * (i + 1)) / 8; ++r) read_part(nbuf, 0, f0, r >> 1, r & 1);
+#pragma unroll
+            for (int d = (13 * i) / 8; d < (13 * (i + 1)) / 8; ++d) dma_op(kt + 3, buf, d);
+            TFQ_FENCE();
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) f_prev[mi] = f_cur[mi] * sbv;
+        buf = nbuf;
+    }
+#undef TFQ_FENCE
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[mi][ni][e] = __builtin_fmaf(tmp[mi][ni][e], f_prev[mi], acc[mi][ni][e]);
+
+    // ---- epilogue: lane holds row wm*128 + mi*32 + fr and columns
+    // wn*64 + ni*32 + 8q + 4h + (0..3) in registers 4q..4q+3.  Bias is always
+    // added (-0.0 without one leaves every value unchanged). ----
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the last block
     lds_barrier();
-    uint8_t* stg = smem + wave * 128 * QEPITCH;
+    const bool has_bias = p.bias != nullptr;
+    const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + XB_BIAS);
+    uint8_t* stg = smem + wave_u * 128 * QEPITCH;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int c0 = n0 + wn * 64 + ni * 32 + 8 * q + 4 * h;
-            float bc[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bc[j] = (p.bias != nullptr && c0 + j < p.n) ? bf16_to_f32(p.bias[c0 + j]) : 0.0f;
+            const int lc0 = wn * 64 + ni * 32 + 8 * q + 4 * h;
+            const uint2 b2 = *reinterpret_cast<const uint2*>(lds_bias + lc0);
+            const float bc[4] = {has_bias ? __uint_as_float(b2.x << 16) : -0.0f,
+                                 has_bias ? __uint_as_float(b2.x & 0xffff0000u) : -0.0f,
+                                 has_bias ? __uint_as_float(b2.y << 16) : -0.0f,
+                                 has_bias ? __uint_as_float(b2.y & 0xffff0000u) : -0.0f};
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    v[j] = acc[mi][ni][4 * q + j];
-                    if (p.bias != nullptr) v[j] = add_bias(v[j], bc[j]);
+                    v[j] = add_bias(acc[mi][ni][4 * q + j], bc[j]);
                     if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
                 }
-                const uint32_t lo = pack_bf16x2(v[0], v[1]);
-                const uint32_t hi = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH +
-                                          (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * QEPITCH + (ni * 32 + 8 * q + 4 * h) * 2) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
         }
     }

@@ -97,6 +97,7 @@ def test_gemm_validation(L):
     assert f(A, B, C, D, 0, 64, 64, 0, None, 0, E, None) == SHAPE
     assert f(A, B, C, D, 64, 64, 64, 64, None, 0, E, None) == UNSUP  # scale_block
     assert f(A, B, C, D, 64, 64, 192, 128, None, 0, E, None) == SHAPE
+    assert f(A, B, C, D, 64, 128, 131072 + 128, 128, None, 0, E, None) == SHAPE  # block-mode k bound
     assert f(A, B, C, D, 64, 64, 64, 0, None, 5, E, None) == UNSUP  # epilogue
     assert f(A + 4, B, C, D, 64, 64, 64, 0, None, 0, E, None) == ALIGN
     assert f(A, B, C, D, 64, 64, 64, 0, None, 0, A + 16, None) == ALIAS
