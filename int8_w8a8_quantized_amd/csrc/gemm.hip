@@ -385,44 +385,44 @@ void gemm_pipe_kernel(const Params p)
         // with 16-byte stores.
         lds_barrier();  // every wave is done with the pipeline buffers
         uint8_t* stg = smem + wave * 128 * EPITCH;
-        // one branch-free pass per bias case
-        auto stage = [&](auto has_bias) {
-            constexpr bool HB = decltype(has_bias)::value;
+        // The column scales and bias values of a column tile are read from LDS
+        // together, with one wait, so that the arithmetic is not broken up by
+        // waits (LDS operations complete in order: a wait for a read also
+        // waits for the staging writes issued before it).  Bias is always
+        // added: without one it is -0.0, which leaves every value (signed
+        // zeros, infinities and NaNs included) unchanged.
+        const bool has_bias = p.bias != nullptr;
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
+        for (int ni = 0; ni < 4; ++ni) {
+            v4f sc[4];
+            uint2 braw[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int lc0 = wn * 128 + ni * 32 + 8 * q + 4 * h;
-                    const v4f sc = *reinterpret_cast<const v4f*>(lds_sb + lc0);
-                    float bc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (HB) {
-                        const uint2 b2 = *reinterpret_cast<const uint2*>(lds_bias + lc0);
-                        bc[0] = __uint_as_float(b2.x << 16);
-                        bc[1] = __uint_as_float(b2.x & 0xffff0000u);
-                        bc[2] = __uint_as_float(b2.y << 16);
-                        bc[3] = __uint_as_float(b2.y & 0xffff0000u);
+            for (int q = 0; q < 4; ++q) {
+                const int lc0 = wn * 128 + ni * 32 + 8 * q + 4 * h;
+                sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
+                braw[q] = *reinterpret_cast<const uint2*>(lds_bias + lc0);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 b2 = braw[q];
+                const float bc[4] = {has_bias ? __uint_as_float(b2.x << 16) : -0.0f,
+                                     has_bias ? __uint_as_float(b2.x & 0xffff0000u) : -0.0f,
+                                     has_bias ? __uint_as_float(b2.y << 16) : -0.0f,
+                                     has_bias ? __uint_as_float(b2.y & 0xffff0000u) : -0.0f};
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[j] = add_bias(scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[q][j]), bc[j]);
+                        if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
                     }
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi) {
-                        float v[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[j]);
-                            if constexpr (HB) v[j] = add_bias(v[j], bc[j]);
-                            if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
-                        }
-                        const uint32_t lo = pack_bf16x2(v[0], v[1]);
-                        const uint32_t hi = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH +
-                                                  (ni * 32 + 8 * q + 4 * h) * 2) = make_uint2(lo, hi);
-                    }
+                    *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH + (ni * 32 + 8 * q + 4 * h) * 2) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
             }
-        };
-        if (p.bias != nullptr)
-            stage(std::true_type{});
-        else
-            stage(std::false_type{});
+        }
         // the wave reads back only what it wrote itself
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int ch = lane & 15;
