@@ -128,6 +128,29 @@ def test_fp8_block_scaled(tfq, M, N, K):
     assert np.array_equal(host_bits(y2), host_bits(y))
 
 
+@pytest.mark.parametrize("M,N,K,epi", [(520, 384, 640, "gelu_tanh"), (300, 256, 256, None),
+                                       (257, 128, 384, "gelu_tanh")])
+def test_fp8_block_scaled_bias_epilogue(tfq, M, N, K, epi):
+    """Block mode with a bias (and GELU): several K blocks, fewer blocks than
+    the kernel's load pipeline is deep, ragged M."""
+    rng = np.random.default_rng(7 * M + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= np.exp2(rng.integers(-3, 3, (1, K // 128))).repeat(128, axis=1).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.03).astype(np.float32)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32)
+    xb, wb, bb = synth.to_bf16_bits(x), synth.to_bf16_bits(w), synth.to_bf16_bits(bias)
+    say(f"block-scaled fp8 + bias M={M} N={N} K={K} epi={epi}")
+    qa, sa = tfq.tfq_quantize_rows(dev_bf16(xb), "fp8", 448.0, 128)
+    qb, sb = tfq.tfq_quantize_weight_per_channel(dev_bf16(wb), "fp8", 448.0, 128)
+    y = tfq.tfq_scaled_mm_fp8(qa, sa, qb, sb, 128, dev_bf16(bb), epi)
+    torch.cuda.synchronize()
+    qa_e, sa_e = orc.quantize_rows(xb, "fp8", 448.0, 128)
+    qb_e, sb_e = orc.quantize_blocks(wb, "fp8", 448.0, 128)
+    ref = orc.linear_ref(qa_e, sa_e, qb_e, sb_e, "fp8", scale_block=128, bias=bb,
+                         gelu=epi == "gelu_tanh")
+    assert_fp8_tolerance(host_bits(y), ref, f"block+bias M={M} N={N} K={K} epi={epi}")
+
+
 @pytest.mark.parametrize("qtype,qmax", [("fp8", 448.0), ("fp8", 7.0), ("int8", 127.0)])
 def test_fused_linear_matches_two_calls_and_oracle(tfq, qtype, qmax):
     M, N, K = 333, 264, 528
