@@ -25,7 +25,7 @@
 //    stores;
 //  * tile order: consecutive workgroup ids go round-robin over the 8 XCDs,
 //    so ids are remapped to give each XCD a contiguous slice of the tile
-//    sequence, which walks bands of 4 tile rows so that the tiles in flight
+//    sequence, which walks bands of 2 or 4 tile rows so that the tiles in flight
 //    on one XCD share A and B panels in that XCD's L2;
 //  * epilogue arithmetic: FP32 (acc * s_a) * s_b [+ bias] [GELU-tanh] -> BF16
 //    (RNE), each step rounded on its own; the INT8 path converts the exact
@@ -47,7 +47,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;  // output tile of the per-token / per-channel kernel
-constexpr int GROUP_M = 4;
 
 struct Params {
     const uint8_t* a;
@@ -59,18 +58,19 @@ struct Params {
     int32_t* acc;
     int m, n, k;
     int tiles_m, tiles_n;
+    int group_m;  // tile rows per band of the tile order
 };
 
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn)
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
 {
     const int total = tiles_m * tiles_n;
     const int full = total & ~7;
     int id = bid;
     if (bid < full) id = (bid & 7) * (full >> 3) + (bid >> 3);
-    const int band_tiles = GROUP_M * tiles_n;
+    const int band_tiles = group_m * tiles_n;
     const int band = id / band_tiles;
-    const int first = band * GROUP_M;
-    const int gm = min(tiles_m - first, GROUP_M);
+    const int first = band * group_m;
+    const int gm = min(tiles_m - first, group_m);
     const int in = id - band * band_tiles;
     tm = first + in % gm;
     tn = in / gm;
@@ -198,7 +198,7 @@ void gemm_pipe_kernel(const Params p)
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.k;
     const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
@@ -485,7 +485,7 @@ void gemm_block_kernel(const Params p)
     const int wm = wave_u & 1, wn = wave_u >> 1;
     const int lane = lane_id_here();
     int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * QBN;
     const int K = p.k;
     const int KT = K >> 7;  // K blocks = stages (K % 128 == 0)
@@ -714,7 +714,7 @@ void gemm_dual_kernel(const Params p)
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * QBN;
     const int K = p.k;
     const int rows_a = min(BM, p.m - m0), rows_b = min(QBN, p.n - n0);
@@ -914,6 +914,19 @@ hipError_t launch_pipe(const Params& p, hipStream_t st)
     return hipGetLastError();
 }
 
+// Tile rows per band of the tile order (see map_tile).  The 32 tiles in
+// flight on one XCD cover about band x (32 / band) tiles; their A row panels
+// stream from HBM while the B (weight) panels mostly hit the Infinity Cache.
+// With long K (a 256-row A panel of 2 MB or more) fewer concurrent A panels
+// win: measured on MI355X, K = 13824 runs best with bands of 2 (2.44 vs 2.34
+// PFLOP/s with 4), K = 3072 and 5120 with bands of 4.
+int band_rows(int64_t m, int64_t n, int64_t k)
+{
+    (void)m;
+    (void)n;
+    return k >= 8192 ? 2 : 4;
+}
+
 }  // namespace
 
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
@@ -931,6 +944,7 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.k = (int)g.k;
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
+    p.group_m = band_rows(g.m, g.n, g.k);
     if (g.scale_block == 128)
         return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
     // Kernel choice by shape: with fewer 256x256 tiles than the 256 CUs the
