@@ -158,6 +158,52 @@ __global__ __launch_bounds__(256) void quantize_rows_resident(
     }
 }
 
+// Long rows resident in registers, WPR waves per row: each wave holds CH
+// chunks of 64 x 8 elements of its part of the row; the row absmax is
+// combined across the row's waves through LDS.  Shorter per-wave register
+// footprints than one wave per row keep more rows in flight.  Arithmetic as
+// in quantize_rows_resident, so results are identical.
+template <int QT, int CH, int WPR>
+__global__ __launch_bounds__(256) void quantize_rows_split(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+    uint8_t* __restrict__ q, float* __restrict__ scale)
+{
+    __shared__ uint32_t part_max[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int part = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+    const bool valid = row < rows;  // every wave reaches the barrier
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (valid ? row : 0) * ld);
+    const int nchunk = (int)(cols >> 3);
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = (part * CH + c) * 64 + lane;
+        v[c] = (valid && idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) m = abs_max_chunk(m, v[c]);
+    m = max(m & 0xFFFFu, m >> 16);
+    m = wave_max(m);
+    if (lane == 0) part_max[wave] = m;
+    __syncthreads();
+    uint32_t mw = 0;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) mw = max(mw, part_max[wave - part + w]);
+    if (!valid) return;
+    const float amax = __uint_as_float(mw << 16);
+    const float s = amax / qmax;  // correctly rounded (IEEE division)
+    if (part == 0 && lane == 0) scale[row] = s;
+    const Quotient d(s);
+    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = (part * CH + c) * 64 + lane;
+        if (idx < nchunk) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
+    }
+}
+
 // Per-row quantisation of long rows: an absmax pass, then a second read.
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_rows_two_pass(
@@ -274,6 +320,17 @@ hipError_t launch_resident(const uint16_t* x, int64_t rows, int64_t cols, int64_
     return hipGetLastError();
 }
 
+template <int QT, int CH, int WPR>
+hipError_t launch_split(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
+                        uint8_t* q, float* s, hipStream_t st)
+{
+    const int64_t rpb = 4 / WPR;
+    const int64_t blocks = (rows + rpb - 1) / rpb;
+    hipLaunchKernelGGL((quantize_rows_split<QT, CH, WPR>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       x, rows, cols, ld, qmax, q, s);
+    return hipGetLastError();
+}
+
 template <int QT>
 hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
                           uint8_t* q, float* s, hipStream_t st)
@@ -286,11 +343,14 @@ hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     if (per_lane <= 8) return launch_resident<QT, 8>(x, rows, cols, ld, qmax, q, s, st);
     if (per_lane <= 10) return launch_resident<QT, 10>(x, rows, cols, ld, qmax, q, s, st);
     if (per_lane <= 12) return launch_resident<QT, 12>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 16) return launch_resident<QT, 16>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 20) return launch_resident<QT, 20>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 24) return launch_resident<QT, 24>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 28) return launch_resident<QT, 28>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 32) return launch_resident<QT, 32>(x, rows, cols, ld, qmax, q, s, st);
+    // longer rows: 2 waves per row up to 16384 columns, 4 up to 32768
+    if (per_lane <= 16) return launch_split<QT, 8, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 20) return launch_split<QT, 10, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 24) return launch_split<QT, 12, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 28) return launch_split<QT, 14, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 32) return launch_split<QT, 16, 2>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 48) return launch_split<QT, 12, 4>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 64) return launch_split<QT, 16, 4>(x, rows, cols, ld, qmax, q, s, st);
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL((quantize_rows_two_pass<QT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
                        rows, cols, ld, qmax, q, s);
