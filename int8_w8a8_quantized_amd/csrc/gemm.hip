@@ -78,14 +78,9 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    // v_cvt_pk_bf16_f32: round-to-nearest-even
-    return __builtin_bit_cast(uint16_t, __float2bfloat16(f));
-}
 
-// two floats -> two BF16 (RNE) in one 32-bit word, lo in the low half: one
-// v_cvt_pk_bf16_f32
+// two floats -> two BF16 (round to nearest even) in one 32-bit word, lo in
+// the low half: one v_cvt_pk_bf16_f32
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -521,7 +516,6 @@ void gemm_block_kernel(const Params p)
         lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
                  lds_base + XB_SA + buf * 1024 + wave_u * 256);
     };
-    constexpr int DMA_PER_STAGE = 13;  // per wave: 8 A + 4 B + 1 row-scale load
 
     // LDS -> fragments: K step ks (0, 1) of a stage, lane reads row
     // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1

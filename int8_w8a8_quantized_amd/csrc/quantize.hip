@@ -268,7 +268,8 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 // 128x128 weight blocks: one workgroup (256 threads) per block.
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_blocks128(
-    const uint16_t* __restrict__ w, int64_t n, int64_t k, float qmax, uint8_t* __restrict__ q,
+    const uint16_t* __restrict__ w, int64_t /* n: the grid covers its n/128 blocks */, int64_t k,
+    float qmax, uint8_t* __restrict__ q,
     float* __restrict__ scale)
 {
     __shared__ uint32_t red[4];
