@@ -78,6 +78,12 @@ def lib():
         L.tfq_oracle_linear_ref.restype = None
         L.tfq_oracle_linear_ref.argtypes = [P, P, P, P, ctypes.c_int, i64, i64, i64, i64, P,
                                             ctypes.c_int, P, i64, P]
+        L.tfq_oracle_mx_scale_code.restype = ctypes.c_uint8
+        L.tfq_oracle_mx_scale_code.argtypes = [ctypes.c_float]
+        L.tfq_oracle_quantize_mx.restype = None
+        L.tfq_oracle_quantize_mx.argtypes = [P, i64, i64, i64, P, P]
+        L.tfq_oracle_linear_mx_ref.restype = None
+        L.tfq_oracle_linear_mx_ref.argtypes = [P, P, P, P, i64, i64, i64, P, ctypes.c_int, P, i64, P]
         L.tfq_oracle_int8_linear.restype = None
         L.tfq_oracle_int8_linear.argtypes = [P, P, P, P, i64, i64, i64, P, P, i64, P, P]
         L.tfq_oracle_error_measures.restype = None
@@ -226,6 +232,41 @@ def linear_ref(a_q, a_scale, b_q, b_scale, qtype, scale_block: int = 0, bias=Non
     lib().tfq_oracle_linear_ref(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _qtype(qtype), M, N, K,
                                 int(scale_block), _ptr(bi), 1 if gelu else 0, _ptr(r), nr,
                                 _ptr(out))
+    return out
+
+
+def mx_scale_code(amax: float) -> int:
+    """E8M0 byte of a 32-element block with largest magnitude amax (OCP MX v1.0 rule)."""
+    return int(lib().tfq_oracle_mx_scale_code(float(amax)))
+
+
+def quantize_mx(x_bf16: np.ndarray):
+    """MXFP8 quantisation of BF16 rows: (codes uint8 [R, C], E8M0 scales uint8 [R, C/32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    R, C = x.shape
+    assert C % 32 == 0
+    q = np.empty((R, C), dtype=np.uint8)
+    s = np.empty((R, C // 32), dtype=np.uint8)
+    lib().tfq_oracle_quantize_mx(_ptr(x), R, C, C, _ptr(q), _ptr(s))
+    return q, s
+
+
+def linear_mx_ref(a_q, a_scale, b_q, b_scale, bias=None, gelu: bool = False, rows=None) -> np.ndarray:
+    """MXFP8 Linear reference y [R, N] in binary64 (see tfq_oracle_linear_mx_ref)."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    b = np.ascontiguousarray(b_q).view(np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and K % 32 == 0
+    sa = np.ascontiguousarray(a_scale, dtype=np.uint8)
+    sb = np.ascontiguousarray(b_scale, dtype=np.uint8)
+    assert sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    out = np.empty((R, N), dtype=np.float64)
+    lib().tfq_oracle_linear_mx_ref(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(bi),
+                                   1 if gelu else 0, _ptr(r), nr, _ptr(out))
     return out
 
 

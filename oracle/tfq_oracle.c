@@ -349,6 +349,94 @@ void tfq_oracle_linear_ref(const uint8_t* a, const float* a_scale, const uint8_t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP8 (E4M3FN elements, 32-element blocks along a row, E8M0 block scales) */
+/* ------------------------------------------------------------------------ */
+/* The pages (TeleFuser "Quantization", converter section; TeleFuser "量化"
+ * page, 离线转换) say only that MXFP4/6/8 use 32-value blocks with E8M0
+ * scales.  The block rule is read from the OCP Microscaling (MX) format
+ * specification v1.0: the shared exponent of a block is
+ * floor(log2(max |v|)) - emax_elem, emax_elem = 8 for E4M3 (448 = 1.75 * 2^8),
+ * clamped to the E8M0 range [-127, 127] (an all-zero block takes -127); the
+ * block scale is X = 2^shared_exp, stored as the E8M0 byte shared_exp + 127;
+ * each element is v / X, clamped to +-448 and encoded to E4M3FN (RNE). */
+
+/* E8M0 byte of a block whose largest magnitude is amax (a finite float). */
+uint8_t tfq_oracle_mx_scale_code(float amax)
+{
+    int e;
+    if (!(amax > 0.0f)) return 0;            /* zero block: 2^-127 */
+    (void)frexpf(amax, &e);                   /* amax = f * 2^e, f in [0.5, 1) */
+    int shared = (e - 1) - 8;                 /* floor(log2 amax) - emax_elem */
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
+/* Quantise rows of BF16 x [rows, cols] (cols % 32 == 0, leading dim ld) to
+ * MXFP8: codes [rows, cols] and E8M0 scales [rows, cols / 32]. */
+void tfq_oracle_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                            uint8_t* q, uint8_t* scale)
+{
+    const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + r * ld + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(tfq_oracle_bf16_to_f32(xb[i]));
+                if (a > amax) amax = a;
+            }
+            const uint8_t code = tfq_oracle_mx_scale_code(amax);
+            scale[r * nb + b] = code;
+            const double X = ldexp(1.0, (int)code - 127);
+            for (int i = 0; i < 32; ++i) {
+                /* v / X is exact in binary64; rounding it to binary32 is the
+                 * only rounding before the E4M3FN encode */
+                float t = (float)((double)tfq_oracle_bf16_to_f32(xb[i]) / X);
+                t = fminf(fmaxf(t, -448.0f), 448.0f);
+                q[r * cols + b * 32 + i] = tfq_oracle_e4m3fn_encode(t);
+            }
+        }
+    }
+}
+
+/* MXFP8 Linear reference in binary64 for selected rows:
+ *   y[m, n] = sum_kb 2^(ea[m,kb] - 127) * 2^(eb[n,kb] - 127) * dot_kb
+ * (dot_kb = the exact binary64 sum of decoded code products over block kb),
+ * then + bias[n] (BF16, may be NULL), then GELU-tanh if epi == 1.  Each
+ * dot_kb is exact; only the combination over blocks rounds (relative error
+ * below K/32 * 2^-53). */
+void tfq_oracle_linear_mx_ref(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                              const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
+                              const uint16_t* bias, int epi, const int64_t* rows, int64_t nrows,
+                              double* y)
+{
+    const int64_t R = rows ? nrows : M;
+    const int64_t nb = K / 32;
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < R; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+        for (int64_t k = 0; k < K; ++k) arow[k] = tfq_oracle_e4m3fn_value(a[m * K + k]);
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            for (int64_t kb = 0; kb < nb; ++kb) {
+                double acc = 0.0;
+                for (int64_t k = kb * 32; k < kb * 32 + 32; ++k)
+                    acc += arow[k] * tfq_oracle_e4m3fn_value(b[n * K + k]);
+                v += ldexp(acc, (int)a_scale[m * nb + kb] - 127 + (int)b_scale[n * nb + kb] - 127);
+            }
+            if (bias) v += (double)tfq_oracle_bf16_to_f32(bias[n]);
+            if (epi == 1) v = tfq_oracle_gelu_tanh(v);
+            y[i * N + n] = v;
+        }
+        free(arow);
+    }
+}
+
 /* INT8 W8A8: exact INT32 accumulators (held in int64 here; the caller keeps
  * K small enough that they fit INT32) and the fixed-order BF16 output.
  * acc and y_bf16 may each be NULL. */
