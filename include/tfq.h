@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 1
+#define TFQ_ABI_VERSION 2
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -194,6 +194,50 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
  * the conversion the quantiser uses can be checked over all binary32 inputs.
  *   x [n] FP32, q [n] codes, both 16-byte aligned; n >= 1, n % 4 == 0.
  */
+/*
+ * MXFP8 quantisation: E4M3FN codes with one E8M0 scale byte per 32
+ * consecutive elements of a row.  TeleFuser "Quantization", converter
+ * section (MXFP8 uses 32-value blocks with E8M0 scales); the pages print no
+ * block rule, so the OCP Microscaling (MX) v1.0 one is used: shared exponent
+ * floor(log2(amax)) - 8 (8 = the exponent of E4M3FN's largest normal),
+ * clamped to [-127, 127], scale byte = shared + 127 (an all-zero block gets
+ * byte 0); codes = E4M3FN_RNE(clamp(x * 2^-shared, -448, 448)), an exact
+ * power-of-two scaling.
+ *
+ *   x_bf16    [rows, cols] BF16, row stride ld_x elements (ld_x >= cols,
+ *             ld_x % 8 == 0), 16-byte aligned.
+ *   q_out     [rows, cols] E4M3FN codes, dense, 16-byte aligned.
+ *   scale_out [cols/128, rows] 32-bit scale words, 4-byte aligned: byte j
+ *             (little-endian) of word (g, r) is the scale of block 4 g + j
+ *             of row r, i.e. the four block scales of a 128-wide K group,
+ *             stored group-major so that the GEMM reads a tile's scales for
+ *             one K group in one piece.
+ *   rows >= 1; cols >= 128, cols % 128 == 0; rows * cols / 32 <= 2^30.
+ * Quantising weights [n, k] with this call gives the MXFP8 weight operand.
+ */
+tfq_status tfq_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                           void* q_out, uint32_t* scale_out, void* stream);
+
+/*
+ * MXFP8 GEMM: y[m,n] = sum over 32-blocks kb of 2^(ea[m,kb] - 127)
+ * 2^(eb[n,kb] - 127) sum_{k in kb} a[m,k] b[n,k], accumulated in FP32 (the
+ * matrix cores apply the E8M0 scales), rounded once to BF16 (RNE), bias
+ * and epilogue as for tfq_scaled_mm_fp8.  TeleFuser "Quantization",
+ * converter section (MXFP8 block format).
+ *
+ *   a_q [m, k], b_q [n, k] E4M3FN codes, K-contiguous, 16-byte aligned.
+ *   a_scale [k/128, m], b_scale [k/128, n] scale words in the layout
+ *   tfq_quantize_mx writes, 4-byte aligned (byte 255, NaN in the MX format,
+ *   gives unspecified results).
+ *   bias_bf16 [n] BF16 or NULL; epi tfq_epilogue; y_bf16 [m, n] BF16,
+ *   16-byte aligned.
+ *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 4194304, k % 128 == 0;
+ *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
+ */
+tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
+                               const uint32_t* b_scale, int64_t m, int64_t n, int64_t k,
+                               const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
+
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream);
 
 /* Static, NUL-terminated description of a status code. */

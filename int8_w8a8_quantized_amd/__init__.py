@@ -22,7 +22,8 @@ from ._lib import TfqError, check, lib
 __all__ = [
     "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
-    "tfq_quant_linear_fused", "tfq_e4m3fn_encode_f32", "tfq_abi_version", "QuantLinear",
+    "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
+    "tfq_abi_version", "QuantLinear",
 ]
 
 QTYPE = {"fp8": 0, "e4m3fn": 0, "int8": 1}
@@ -141,6 +142,35 @@ def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0
                                        float(act_qmax), int(scale_block), _ptr(bias), _epi(epi),
                                        _ptr(y), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "tfq_quant_linear_fused")
+    return y
+
+
+def tfq_quantize_mx(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
+    """MXFP8 quantisation of BF16 rows x [rows, cols] (row stride x.stride(0)):
+    returns (E4M3FN codes [rows, cols], E8M0 scales as uint8
+    [cols/128, rows, 4]: entry (g, r, j) is the scale of block 4 g + j of
+    row r)."""
+    rows, cols = x.shape
+    if q_out is None:
+        q_out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=x.device)
+    check(lib().tfq_quantize_mx(_ptr(x), rows, cols, x.stride(0), _ptr(q_out), _ptr(scale_out),
+                                _stream(stream)), "tfq_quantize_mx")
+    return q_out, scale_out
+
+
+def tfq_scaled_mm_mxfp8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None, stream=None):
+    """y [m, n] BF16 from MXFP8 operands a_q [m, k], b_q [n, k] with E8M0
+    block scales in the layout tfq_quantize_mx returns ([k/128, m, 4] and
+    [k/128, n, 4])."""
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    check(lib().tfq_scaled_mm_mxfp8(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n, k,
+                                    _ptr(bias), _epi(epi), _ptr(y), _stream(stream)),
+          "tfq_scaled_mm_mxfp8")
     return y
 
 

@@ -133,6 +133,10 @@ tfq_status validate_gemm(const void* a, const float* sa, const void* b, const fl
     return TFQ_OK;
 }
 
+// MXFP8 scale words [k/128, rows]: word offsets must fit the GEMM's 32-bit
+// buffer offsets
+bool mx_scales_fit(int64_t rows, int64_t k) { return rows * (k / 32) <= ((int64_t)1 << 30); }
+
 size_t workspace_bytes(int64_t m, int64_t k, int32_t block)
 {
     const int64_t ns = block == 128 ? m * (k / 128) : m;
@@ -280,6 +284,49 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
     tfq::GemmArgs g{codes, (const uint8_t*)w_q, scales, w_scale, (const uint16_t*)bias_bf16,
                     (uint16_t*)y_bf16, nullptr, m, n, k, qtype, scale_block, epi};
     return hip_status(tfq::launch_scaled_gemm(g, s));
+}
+
+tfq_status tfq_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                           void* q_out, uint32_t* scale_out, void* stream)
+{
+    if (!x_bf16 || !q_out || !scale_out) return TFQ_ERR_NULL_POINTER;
+    if (rows < 1 || rows > kMaxDim || cols < 128 || cols > kMaxDim || cols % 128 != 0 ||
+        ld_x < cols || ld_x > kMaxDim || !mx_scales_fit(rows, cols))
+        return TFQ_ERR_BAD_SHAPE;
+    if (ld_x % 8 != 0 || !aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(scale_out, 4))
+        return TFQ_ERR_MISALIGNED;
+    const Range rx = range_of(x_bf16, ((rows - 1) * ld_x + cols) * 2);
+    const Range rq = range_of(q_out, rows * cols), rs = range_of(scale_out, rows * (cols / 32));
+    if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    return hip_status(tfq::launch_quantize_mx((const uint16_t*)x_bf16, rows, cols, ld_x,
+                                              (uint8_t*)q_out, scale_out, (hipStream_t)stream));
+}
+
+tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
+                               const uint32_t* b_scale, int64_t m, int64_t n, int64_t k,
+                               const void* bias_bf16, int32_t epi, void* y_bf16, void* stream)
+{
+    if (!a_q || !a_scale || !b_q || !b_scale || !y_bf16) return TFQ_ERR_NULL_POINTER;
+    if (!epi_ok(epi)) return TFQ_ERR_UNSUPPORTED;
+    if (m < 1 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 || k < 128 ||
+        k > ((int64_t)1 << 22) || k % 128 != 0 || !mx_scales_fit(m, k) || !mx_scales_fit(n, k))
+        return TFQ_ERR_BAD_SHAPE;
+    if (((m + 255) / 256) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
+        (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        return TFQ_ERR_MISALIGNED;
+    const Range ry = range_of(y_bf16, m * n * 2);
+    const Range ins[5] = {range_of(a_q, m * k), range_of(b_q, n * k), range_of(a_scale, m * (k / 32)),
+                          range_of(b_scale, n * (k / 32)), range_of(bias_bf16, bias_bf16 ? n * 2 : 0)};
+    for (const Range& r : ins)
+        if (overlap(r, ry)) return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    tfq::GemmArgs g{a_q, b_q, nullptr, nullptr, (const uint16_t*)bias_bf16, (uint16_t*)y_bf16,
+                    nullptr, m, n, k, tfq::kMxE4M3, 0, epi, a_scale, b_scale};
+    return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
 }
 
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream)

@@ -53,6 +53,8 @@ struct Params {
     const uint8_t* b;
     const float* sa;
     const float* sb;
+    const uint32_t* ea;  // MXFP8 E8M0 scale words [k/128, m]
+    const uint32_t* eb;  // MXFP8 E8M0 scale words [k/128, n]
     const uint16_t* bias;
     uint16_t* y;
     int32_t* acc;
@@ -129,7 +131,10 @@ constexpr int PBUF = 2;               // LDS buffers: stages in flight
 // the tile's row scales, column scales and BF16 bias (1 KB each) sit past
 // both the pipeline buffers and the output staging area
 constexpr int PSCL = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
-constexpr int PSMEM = PSCL + 3 * 1024;
+// MXFP8: the E8M0 scales of two stages (A rows, then B rows; 4 bytes = the
+// stage's 4 K blocks per row)
+constexpr int PMXS = PSCL + 3 * 1024;
+constexpr int PSMEM = PMXS + 2 * 2048;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -173,6 +178,15 @@ __device__ __forceinline__ int lane_id_here()
     return l;
 }
 
+// 64 lanes x 4 bytes from the buffer at per-lane byte offset `off` straight
+// into LDS [lds, lds + 256), lane l at lds + 4 l (caller orders with vmcnt)
+__device__ __forceinline__ void lds_dma4(const v4i& rsrc, int off, uint32_t lds)
+{
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
 template <int QT>
 struct PipeAcc;
 template <>
@@ -182,6 +196,10 @@ struct PipeAcc<kE4M3FN> {
 template <>
 struct PipeAcc<kInt8> {
     typedef v16i type;
+};
+template <>
+struct PipeAcc<kMxE4M3> {
+    typedef v16f type;
 };
 
 template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
@@ -217,13 +235,21 @@ void gemm_pipe_kernel(const Params p)
     const int row_off = (64 * wave + (lane >> 3)) * K;
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
     // LDS -> fragments: for K step ks (0, 1) of a stage, lane reads row
-    // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1
+    // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1 into
+    // registers 0-3 and 4-7.  MXFP8 reads chunks 4 ks + h and 4 ks + 2 + h
+    // instead: the scaled MFMA applies one block scale to registers 0-3 of
+    // both lane halves and another to registers 4-7 (the scale of the first
+    // comes from lanes 0-31, of the second from lanes 32-63), so each of
+    // those register groups must hold one whole 32-element block.
     const int fr = lane & 31, h = lane >> 5, sw = (fr >> 1) & 7;
     int rd[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) rd[ks][e] = fr * PK + (((4 * ks + 2 * h + e) ^ sw) << 4);
+        for (int e = 0; e < 2; ++e) {
+            const int ch = QT == kMxE4M3 ? 4 * ks + h + 2 * e : 4 * ks + 2 * h + e;
+            rd[ks][e] = fr * PK + ((ch ^ sw) << 4);
+        }
     const int a_rd = wm * 128 * PK;
     const int b_rd = PA + wn * 128 * PK;
     const int KT = (K + PK - 1) / PK;
@@ -263,10 +289,24 @@ void gemm_pipe_kernel(const Params p)
     };
     // weights as the first operand: the 32x32 result is the transposed
     // output tile, so each lane ends up with 4 consecutive columns
-    auto mfma_one = [&](int mi, int ni, const Frags& f) {
+    // MXFP8: the block scales of K step ks are blocks 2 ks (registers 0-3,
+    // taken from lanes 0-31) and 2 ks + 1 (registers 4-7, from lanes 32-63):
+    // lane half h passes byte 2 ks + h of its row's scale dword.  The dword
+    // is kept shifted right by 8 h, so the MFMA's byte select is 2 ks for
+    // every lane (operand order as the data).
+    constexpr bool MX = QT == kMxE4M3;
+    int scA[2][4], scB[2][4];
+    auto mfma_one = [&](int mi, int ni, const Frags& f, int set = 0, int ks = 0) {
         if constexpr (QT == kE4M3FN) {
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, 0, 0, 0);
+        } else if constexpr (MX) {
+            if (ks == 0)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, scB[set][ni], 0, scA[set][mi]);
+            else
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 2, scB[set][ni], 2, scA[set][mi]);
         } else {
             const v8i b8 = f.b[ni], a8 = f.a[mi];
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
@@ -275,6 +315,30 @@ void gemm_pipe_kernel(const Params p)
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                 v4i{b8[4], b8[5], b8[6], b8[7]}, v4i{a8[4], a8[5], a8[6], a8[7]}, acc[mi][ni],
                 0, 0, 0);
+        }
+    };
+    // MXFP8 scale loads of stage kt: the scale words of a 128-wide K group
+    // are stored group-major, so a tile's 256 row words of one stage are 1 KB
+    // in one piece (wave w loads rows 64 w + lane of A and of B).  Rows past
+    // the end of A or B read the next group's words (finite scales of zero
+    // data, in outputs that are never stored) or zeros past the tensor.
+    const int KG = K / PK;
+    const v4i rea = MX ? buffer_rsrc(p.ea + m0, (KG * p.m - m0) * 4) : v4i{};
+    const v4i reb = MX ? buffer_rsrc(p.eb + n0, (KG * p.n - n0) * 4) : v4i{};
+    auto dma_mx = [&](int kt) {
+        const int r = 64 * wave + lane;
+        const bool pad = kt >= KG;
+        const uint32_t dst = lds_base + PMXS + (kt & 1) * 2048 + wave_u * 256;
+        lds_dma4(rea, pad ? (int)0x80000000u : (kt * p.m + r) * 4, dst);
+        lds_dma4(reb, pad ? (int)0x80000000u : (kt * p.n + r) * 4, dst + 1024);
+    };
+    auto read_mx = [&](int buf, int set) {
+        const uint32_t* sm = reinterpret_cast<const uint32_t*>(smem + PMXS + buf * 2048);
+        const int hsh = 8 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            scA[set][i] = (int)(sm[wm * 128 + i * 32 + fr] >> hsh);
+            scB[set][i] = (int)(sm[256 + wn * 128 + i * 32 + fr] >> hsh);
         }
     };
 #define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -291,27 +355,34 @@ void gemm_pipe_kernel(const Params p)
     Frags f0, f1;
     // waves 0, 1, 2 fetch the tile's row scales, column scales and bias into
     // LDS (past the end: zeros); issued first, so the prologue's wait covers them
-    if (wave_u == 0) {
+    if (wave_u == 0 && !MX) {
         lds_dma16(buffer_rsrc(p.sa + m0, rows_a * 4), lane * 16, lds_base + PSCL);
-    } else if (wave_u == 1) {
+    } else if (wave_u == 1 && !MX) {
         lds_dma16(buffer_rsrc(p.sb + n0, rows_b * 4), lane * 16, lds_base + PSCL + 1024);
     } else if (wave_u == 2 && p.bias != nullptr) {
         lds_dma16(buffer_rsrc(p.bias + n0, rows_b * 2), lane * 16, lds_base + PSCL + 2048);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             dma(u, 0, j);
             dma(u, 1, j);
         }
-    // stage 0 complete: the 16 loads of stage 1 may still be in flight
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        if constexpr (MX) dma_mx(u);
+    }
+    // stage 0 complete: the loads of stage 1 (16, plus 2 scale loads for
+    // MXFP8) may still be in flight
+    if constexpr (MX)
+        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         read_part(0, 0, f0, q, 0);
         read_part(0, 0, f0, q, 1);
     }
+    if constexpr (MX) read_mx(0, 0);
 
     for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
@@ -319,7 +390,7 @@ void gemm_pipe_kernel(const Params p)
             // K step 0 of stage kt+u from f0; K step 1's fragments into f1
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mfma_one(i >> 2, i & 3, f0);
+                mfma_one(i >> 2, i & 3, f0, u, 0);
                 TFQ_FENCE();
                 read_part(u, 1, f1, i >> 1, i & 1);
                 TFQ_FENCE();
@@ -328,15 +399,18 @@ void gemm_pipe_kernel(const Params p)
             asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             // K step 1 from f1; stage kt+u+1's first fragments into f0 and
             // the loads of stage kt+u+2
+            if constexpr (MX) read_mx(u ^ 1, u ^ 1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mfma_one(i >> 2, i & 3, f1);
+                mfma_one(i >> 2, i & 3, f1, u, 1);
                 TFQ_FENCE();
                 read_part(u ^ 1, 0, f0, i >> 1, i & 1);
                 if (i < 8) {
                     dma(kt + u + 2, 0, i);
                     dma(kt + u + 2, 1, i);
                 }
+                if constexpr (MX)
+                    if (i == 8) dma_mx(kt + u + 2);
                 TFQ_FENCE();
             }
         }
@@ -353,9 +427,10 @@ void gemm_pipe_kernel(const Params p)
     const float* lds_sa = reinterpret_cast<const float*>(smem + PSCL);
     const float* lds_sb = reinterpret_cast<const float*>(smem + PSCL + 1024);
     const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + PSCL + 2048);
+    // (MXFP8: the sums are already scaled; no row or column scales)
     float srow[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) srow[mi] = lds_sa[wm * 128 + mi * 32 + fr];
+    for (int mi = 0; mi < 4; ++mi) srow[mi] = MX ? 1.0f : lds_sa[wm * 128 + mi * 32 + fr];
     if constexpr (WANT_ACC) {
         // raw INT32 sums: 16-byte stores of 4 consecutive columns
 #pragma unroll
@@ -394,7 +469,7 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int lc0 = wn * 128 + ni * 32 + 8 * q + 4 * h;
-                sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
+                if constexpr (!MX) sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
                 braw[q] = *reinterpret_cast<const uint2*>(lds_bias + lc0);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -410,7 +485,10 @@ void gemm_pipe_kernel(const Params p)
                     float v[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        v[j] = add_bias(scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[q][j]), bc[j]);
+                        if constexpr (MX)
+                            v[j] = add_bias(acc[mi][ni][4 * q + j], bc[j]);
+                        else
+                            v[j] = add_bias(scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[q][j]), bc[j]);
                         if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
                     }
                     *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH + (ni * 32 + 8 * q + 4 * h) * 2) =
@@ -461,14 +539,6 @@ constexpr int XB_BIAS = XB_SA + XB_BUF * 1024;  // the tile's 128 BF16 bias valu
 constexpr int XB_SB = XB_BIAS + 256;            // the weight block's scales, K/128 <= 1024
 constexpr int XB_SMEM = XB_SB + 4096;
 
-// 64 lanes x 4 bytes from the buffer at per-lane byte offset `off` straight
-// into LDS [lds, lds + 256), lane l at lds + 4 l (caller orders with vmcnt)
-__device__ __forceinline__ void lds_dma4(const v4i& rsrc, int off, uint32_t lds)
-{
-    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
-                 "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory");
-}
 
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -930,6 +1000,8 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.b = g.b;
     p.sa = g.sa;
     p.sb = g.sb;
+    p.ea = g.ea;
+    p.eb = g.eb;
     p.bias = g.bias;
     p.y = g.y;
     p.acc = g.acc;
@@ -941,6 +1013,10 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.group_m = band_rows(g.m, g.n, g.k);
     if (g.scale_block == 128)
         return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
+    // MXFP8 always takes the 256x256 kernel (its scale ring lives there)
+    if (g.qtype == kMxE4M3)
+        return g.epi == 1 ? launch_pipe<kMxE4M3, 1, true, false>(p, stream)
+                          : launch_pipe<kMxE4M3, 0, true, false>(p, stream);
     // Kernel choice by shape: with fewer 256x256 tiles than the 256 CUs the
     // big-tile kernel leaves CUs idle, so the 256x128 two-per-CU kernel takes
     // those problems.  Both sum every output in the same order (same MFMAs,

@@ -265,6 +265,67 @@ __global__ __launch_bounds__(256) void quantize_groups128(
     }
 }
 
+// MXFP8: E4M3FN elements with one E8M0 scale per 32 consecutive elements of
+// a row (TeleFuser "Quantization", converter section: MXFP4/6/8 use 32-value
+// blocks and E8M0 scales).  Block rule of the OCP MX v1.0 format: shared
+// exponent floor(log2(amax)) - 8 (8 = exponent of E4M3's largest normal,
+// 448 = 1.75 * 2^8), clamped to [-127, 127]; E8M0 byte = shared + 127.  For a
+// BF16 amax with exponent field e that byte is max(e - 8, 0) (a subnormal or
+// zero amax has e = 0).  Elements are x * 2^-shared -- an exact power-of-two
+// scaling -- clamped to +-448 and encoded E4M3FN (RNE).  One wave per row; a
+// lane holds 8 elements, 4 lanes one block, 16 lanes one 128-wide K group.
+// The scale bytes of a group go out as one 32-bit word (block 4 g + j in
+// byte j), stored group-major -- word (g, row) at g * rows + row -- the
+// layout the MXFP8 GEMM loads whole per K stage.
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
+                                                          int64_t rows, int64_t cols, int64_t ld,
+                                                          uint8_t* __restrict__ q,
+                                                          uint32_t* __restrict__ scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    const int nchunk = (int)(cols >> 3);  // a multiple of 16: whole groups only
+    constexpr int U = 4;
+    for (int base = 0; base < nchunk; base += 64 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * 64 + lane;
+            v[u] = idx < nchunk ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * 64 + lane;
+            uint32_t m = abs_max_chunk(0u, v[u]);
+            m = max(m & 0xFFFFu, m >> 16);
+            // block max over the 4 lanes of the quad
+            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+            const int code = max((int)((m >> 7) & 0xFFu) - 8, 0);
+            const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
+            // the codes of the group's other 3 blocks (lanes +4, +8, +12 of the
+            // 16-lane DPP row) into the group's first lane
+            const uint32_t word = (uint32_t)code |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 8) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 16) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
+            if (idx < nchunk) {
+                const uint4 w = v[u];
+                uint2 o;
+                o.x = encode4<kE4M3FN>(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv,
+                                       bf_hi(w.y) * inv, 448.0f);
+                o.y = encode4<kE4M3FN>(bf_lo(w.z) * inv, bf_hi(w.z) * inv, bf_lo(w.w) * inv,
+                                       bf_hi(w.w) * inv, 448.0f);
+                qr[idx] = o;
+                if ((lane & 15) == 0) scale[(int64_t)(idx >> 4) * rows + row] = word;
+            }
+        }
+    }
+}
+
 // 128x128 weight blocks: one workgroup (256 threads) per block.
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_blocks128(
@@ -376,6 +437,15 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
     }
     if (qtype == kE4M3FN) return launch_rows_qt<kE4M3FN>(x, rows, cols, ld, qmax, q, scale, stream);
     return launch_rows_qt<kInt8>(x, rows, cols, ld, qmax, q, scale, stream);
+}
+
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* q, uint32_t* scale, hipStream_t stream)
+{
+    const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows,
+                       cols, ld, q, scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int qtype, float qmax,

@@ -8,7 +8,8 @@
 
 namespace tfq {
 
-enum QType : int { kE4M3FN = 0, kInt8 = 1 };
+// kMxE4M3: E4M3FN codes with one E8M0 scale per 32 elements along K (MXFP8)
+enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2 };
 
 // Launchers enqueue kernels on `stream` and return the launch status.  They
 // assume the arguments already passed the host-side validation.
@@ -17,6 +18,13 @@ enum QType : int { kE4M3FN = 0, kInt8 = 1 };
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                 int qtype, float qmax, int group_cols, uint8_t* q, float* scale,
                                 hipStream_t stream);
+
+// MXFP8 rows: E4M3FN codes [rows, cols] and E8M0 scales [rows, cols / 32]
+// (cols % 32 == 0).
+// MXFP8 rows (cols % 128 == 0): codes [rows, cols], E8M0 scale words
+// [cols/128, rows] (byte j of word (g, r) = block 4 g + j of row r)
+hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* q, uint32_t* scale, hipStream_t stream);
 
 // 128x128 block weight quantisation (n % 128 == 0, k % 128 == 0).
 hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int qtype, float qmax,
@@ -37,6 +45,8 @@ struct GemmArgs {
     int qtype;
     int scale_block;       // 0 or 128
     int epi;               // 0 none, 1 gelu-tanh
+    const uint32_t* ea;    // MXFP8: E8M0 scale words [k/128, m] (sa, sb unused), else null
+    const uint32_t* eb;    // MXFP8: E8M0 scale words [k/128, n], else null
 };
 
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);

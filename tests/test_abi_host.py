@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 1
+    assert L.tfq_abi_version() == 2
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -108,6 +108,36 @@ def test_gemm_validation(L):
 
 
 @no_gpu_only
+def test_mx_validation(L):
+    q = L.tfq_quantize_mx
+    assert q(None, 4, 128, 128, B, C, None) == NULL
+    assert q(A, 4, 128, 128, B, None, None) == NULL
+    assert q(A, 0, 128, 128, B, C, None) == SHAPE
+    assert q(A, 4, 96, 96, B, C, None) == SHAPE           # cols % 128
+    assert q(A, 4, 128, 64, B, C, None) == SHAPE          # ld < cols
+    assert q(A, 1 << 24, 4096, 4096, B, C, None) == SHAPE  # scale words past 2^30 bytes
+    assert q(A, 4, 128, 132, B, C, None) == ALIGN         # ld % 8
+    assert q(A + 2, 4, 128, 128, B, C, None) == ALIGN
+    assert q(A, 4, 128, 128, B + 8, C, None) == ALIGN
+    assert q(A, 4, 128, 128, B, C + 2, None) == ALIGN     # scale words: 4 bytes
+    assert q(A, 4, 128, 128, A + 64, C, None) == ALIAS    # codes over x
+    assert q(A, 4, 128, 128, B, B + 508, None) == ALIAS   # scales over codes
+    g = L.tfq_scaled_mm_mxfp8
+    assert g(A, B, C, D, 64, 64, 128, None, 0, None, None) == NULL
+    assert g(A, None, C, D, 64, 64, 128, None, 0, E, None) == NULL
+    assert g(A, B, C, D, 64, 64, 128, None, 2, E, None) == UNSUP   # epilogue
+    assert g(A, B, C, D, 64, 64, 96, None, 0, E, None) == SHAPE    # k % 128
+    assert g(A, B, C, D, 64, 60, 128, None, 0, E, None) == SHAPE   # n % 8
+    assert g(A, B, C, D, 0, 64, 128, None, 0, E, None) == SHAPE
+    assert g(A, B, C, D, 64, 64, (1 << 22) + 128, None, 0, E, None) == SHAPE
+    assert g(A, B, C, D, 1 << 20, 64, 1 << 16, None, 0, E, None) == SHAPE  # a_scale words
+    assert g(A, B + 2, C, D, 64, 64, 128, None, 0, E, None) == ALIGN  # scale words: 4 bytes
+    assert g(A + 4, B, C, D, 64, 64, 128, None, 0, E, None) == ALIGN
+    assert g(A, B, C, D, 64, 64, 128, None, 0, E + 8, None) == ALIGN
+    assert g(A, B, C, D, 64, 64, 128, None, 0, B + 16, None) == ALIAS  # y over a_scale
+
+
+@no_gpu_only
 def test_fused_validation(L):
     ws = L.tfq_quant_linear_workspace_bytes
     need = ws(100, 256, 0, 0)
@@ -129,6 +159,8 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.tfq_quantize_rows(A, 4, 64, 64, 0, 448.0, 0, B, C, None) == DEV
     assert L.tfq_scaled_mm_fp8(A, B, C, D, 64, 64, 64, 0, None, 0, E, None) == DEV
     assert L.tfq_e4m3fn_encode_f32(A, B, 64, None) == DEV
+    assert L.tfq_quantize_mx(A, 4, 128, 128, B, C, None) == DEV
+    assert L.tfq_scaled_mm_mxfp8(A, B, C, D, 64, 64, 128, None, 0, E, None) == DEV
 
 
 def test_python_binding_names_match_abi():
