@@ -172,6 +172,37 @@ def extras(torch, tfq, synth, stream):
     return out
 
 
+def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y):
+    """The same FFN pair in MXFP8 (E8M0 scale per 32 elements, scales applied
+    by the scaled MFMA): each call timed on its own (median of 20)."""
+    log("extras: c4 FFN pair in MXFP8")
+    M, K = x.shape
+    N, N2 = w_up.shape[0], w_dn.shape[0]
+    wq_up, ws_up = tfq.tfq_quantize_mx(w_up)
+    wq_dn, ws_dn = tfq.tfq_quantize_mx(w_dn)
+    qx, sx = tfq.tfq_quantize_mx(x)
+    qg, sg = tfq.tfq_quantize_mx(g)
+    out = {}
+    ms_qx, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_mx(x, qx, sx))
+    ms_up, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_mxfp8(qx, sx, wq_up, ws_up, None,
+                                                                          "gelu_tanh", g))
+    ms_qg, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_mx(g, qg, sg))
+    ms_dn, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_mxfp8(qg, sg, wq_dn, ws_dn, None,
+                                                                          None, y))
+    mxq = lambda m, k: 3 * m * k + m * k // 32  # noqa: E731  (2 B in, 1 B code, 1/32 B scale)
+    fl = 2.0 * M * N * K
+    out["quant_x"] = {"ms": ms_qx, "gbs": mxq(M, K) / ms_qx / 1e6}
+    out["gemm_up_gelu"] = {"ms": ms_up, "tflops": fl / ms_up / 1e9,
+                           "frac_fp8_peak": fl / ms_up / 1e9 / FP8_PEAK_TFLOPS}
+    out["quant_g"] = {"ms": ms_qg, "gbs": mxq(M, N) / ms_qg / 1e6}
+    out["gemm_down"] = {"ms": ms_dn, "tflops": 2.0 * M * N2 * N / ms_dn / 1e9,
+                        "frac_fp8_peak": 2.0 * M * N2 * N / ms_dn / 1e9 / FP8_PEAK_TFLOPS}
+    step = ms_qx + ms_up + ms_qg + ms_dn
+    out["step_ms_sum_of_medians"] = step
+    out["step_tflops"] = 4.0 * M * N * K / step / 1e9
+    return out
+
+
 def cpu_baseline(d, rows_sample: int):
     """The oracle on host cores over a row sample of the same FFN-pair step:
     quantise the sampled X rows, up GEMM + GELU, BF16 round, quantise G rows,
@@ -311,9 +342,11 @@ def main():
 
     ext = {}
     if not args.no_extras:
+        ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y)
+        torch.cuda.synchronize()
         del x, g, qg, y, qx
         torch.cuda.empty_cache()
-        ext = extras(torch, tfq, synth, stream)
+        ext.update(extras(torch, tfq, synth, stream))
 
     cpu = None
     if not args.no_cpu:
