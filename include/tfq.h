@@ -207,11 +207,12 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
  *   x_bf16    [rows, cols] BF16, row stride ld_x elements (ld_x >= cols,
  *             ld_x % 8 == 0), 16-byte aligned.
  *   q_out     [rows, cols] E4M3FN codes, dense, 16-byte aligned.
- *   scale_out [cols/128, rows] 32-bit scale words, 4-byte aligned: byte j
- *             (little-endian) of word (g, r) is the scale of block 4 g + j
- *             of row r, i.e. the four block scales of a 128-wide K group,
- *             stored group-major so that the GEMM reads a tile's scales for
- *             one K group in one piece.
+ *   scale_out [cols/128, rows] 32-bit scale words, 4-byte aligned: bytes
+ *             0, 1, 2, 3 (little-endian) of word (g, r) are the scales of
+ *             blocks 4 g, 4 g + 2, 4 g + 1, 4 g + 3 of row r -- the four
+ *             block scales of a 128-wide K group, stored group-major so that
+ *             the GEMM reads a tile's scales for one K group in one piece,
+ *             in the byte order its matrix instructions take them.
  *   rows >= 1; cols >= 128, cols % 128 == 0; rows * cols / 32 <= 2^30.
  * Quantising weights [n, k] with this call gives the MXFP8 weight operand.
  */

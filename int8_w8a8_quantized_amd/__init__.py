@@ -148,8 +148,8 @@ def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0
 def tfq_quantize_mx(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
     """MXFP8 quantisation of BF16 rows x [rows, cols] (row stride x.stride(0)):
     returns (E4M3FN codes [rows, cols], E8M0 scales as uint8
-    [cols/128, rows, 4]: entry (g, r, j) is the scale of block 4 g + j of
-    row r)."""
+    [cols/128, rows, 4]: entries (g, r, 0..3) are the scales of blocks
+    4 g, 4 g + 2, 4 g + 1, 4 g + 3 of row r)."""
     rows, cols = x.shape
     if q_out is None:
         q_out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)

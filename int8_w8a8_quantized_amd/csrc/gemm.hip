@@ -131,10 +131,11 @@ constexpr int PBUF = 2;               // LDS buffers: stages in flight
 // the tile's row scales, column scales and BF16 bias (1 KB each) sit past
 // both the pipeline buffers and the output staging area
 constexpr int PSCL = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 128 * EPITCH;
-// MXFP8: the E8M0 scales of two stages (A rows, then B rows; 4 bytes = the
-// stage's 4 K blocks per row)
+// MXFP8: the E8M0 scale words of two stages (A rows, then B rows; one word =
+// the stage's 4 K blocks of a row)
 constexpr int PMXS = PSCL + 3 * 1024;
-constexpr int PSMEM = PMXS + 2 * 2048;
+constexpr int PMXRING = 2;
+constexpr int PSMEM = PMXS + PMXRING * 2048;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -291,9 +292,10 @@ void gemm_pipe_kernel(const Params p)
     // output tile, so each lane ends up with 4 consecutive columns
     // MXFP8: the block scales of K step ks are blocks 2 ks (registers 0-3,
     // taken from lanes 0-31) and 2 ks + 1 (registers 4-7, from lanes 32-63):
-    // lane half h passes byte 2 ks + h of its row's scale dword.  The dword
-    // is kept shifted right by 8 h, so the MFMA's byte select is 2 ks for
-    // every lane (operand order as the data).
+    // lane half h passes the scale of block 2 ks + h of its row.  A scale
+    // word holds the group's blocks in the byte order 0, 2, 1, 3, so lane
+    // half h reads the 16 bits at byte 2 h -- blocks h and 2 + h -- and the
+    // MFMA's byte select is ks for every lane (operand order as the data).
     constexpr bool MX = QT == kMxE4M3;
     int scA[2][4], scB[2][4];
     auto mfma_one = [&](int mi, int ni, const Frags& f, int set = 0, int ks = 0) {
@@ -306,7 +308,7 @@ void gemm_pipe_kernel(const Params p)
                     f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, scB[set][ni], 0, scA[set][mi]);
             else
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 2, scB[set][ni], 2, scA[set][mi]);
+                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 1, scB[set][ni], 1, scA[set][mi]);
         } else {
             const v8i b8 = f.b[ni], a8 = f.a[mi];
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
@@ -328,17 +330,19 @@ void gemm_pipe_kernel(const Params p)
     auto dma_mx = [&](int kt) {
         const int r = 64 * wave + lane;
         const bool pad = kt >= KG;
-        const uint32_t dst = lds_base + PMXS + (kt & 1) * 2048 + wave_u * 256;
+        const uint32_t dst = lds_base + PMXS + (kt & (PMXRING - 1)) * 2048 + wave_u * 256;
         lds_dma4(rea, pad ? (int)0x80000000u : (kt * p.m + r) * 4, dst);
         lds_dma4(reb, pad ? (int)0x80000000u : (kt * p.n + r) * 4, dst + 1024);
     };
-    auto read_mx = [&](int buf, int set) {
-        const uint32_t* sm = reinterpret_cast<const uint32_t*>(smem + PMXS + buf * 2048);
-        const int hsh = 8 * h;
+    // (straight from LDS into the MFMA's scale operand: no VALU work, so the
+    // reads need not complete before the MFMAs that do not use them)
+    auto read_mx = [&](int kt, int set) {
+        const uint16_t* sm =
+            reinterpret_cast<const uint16_t*>(smem + PMXS + (kt & (PMXRING - 1)) * 2048);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            scA[set][i] = (int)(sm[wm * 128 + i * 32 + fr] >> hsh);
-            scB[set][i] = (int)(sm[256 + wn * 128 + i * 32 + fr] >> hsh);
+            scA[set][i] = sm[2 * (wm * 128 + i * 32 + fr) + h];
+            scB[set][i] = sm[2 * (256 + wn * 128 + i * 32 + fr) + h];
         }
     };
 #define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -352,6 +356,12 @@ void gemm_pipe_kernel(const Params p)
     // read after each MFMA, and issues the 16 loads of stage s + 2 into the
     // freed buffer, two after each of its first 8 MFMAs.  The loop runs an
     // even number of stages (a stage past K reads zeros).
+    //
+    // MXFP8 scale words ride along, two 4-byte loads per wave per stage into
+    // a 2-slot ring: stage s + 2's go out first in the second K step of
+    // stage s (into the slot of stage s, whose words every wave has read
+    // before the barrier of stage s).  Issued ahead of the data loads they
+    // measured faster than behind them.
     Frags f0, f1;
     // waves 0, 1, 2 fetch the tile's row scales, column scales and bias into
     // LDS (past the end: zeros); issued first, so the prologue's wait covers them
@@ -399,18 +409,18 @@ void gemm_pipe_kernel(const Params p)
             asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             // K step 1 from f1; stage kt+u+1's first fragments into f0 and
             // the loads of stage kt+u+2
-            if constexpr (MX) read_mx(u ^ 1, u ^ 1);
+            if constexpr (MX) read_mx(kt + u + 1, u ^ 1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 mfma_one(i >> 2, i & 3, f1, u, 1);
                 TFQ_FENCE();
                 read_part(u ^ 1, 0, f0, i >> 1, i & 1);
+                if constexpr (MX)
+                    if (i == 0) dma_mx(kt + u + 2);
                 if (i < 8) {
                     dma(kt + u + 2, 0, i);
                     dma(kt + u + 2, 1, i);
                 }
-                if constexpr (MX)
-                    if (i == 8) dma_mx(kt + u + 2);
                 TFQ_FENCE();
             }
         }

@@ -274,9 +274,11 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 // zero amax has e = 0).  Elements are x * 2^-shared -- an exact power-of-two
 // scaling -- clamped to +-448 and encoded E4M3FN (RNE).  One wave per row; a
 // lane holds 8 elements, 4 lanes one block, 16 lanes one 128-wide K group.
-// The scale bytes of a group go out as one 32-bit word (block 4 g + j in
-// byte j), stored group-major -- word (g, row) at g * rows + row -- the
-// layout the MXFP8 GEMM loads whole per K stage.
+// The scale bytes of a group go out as one 32-bit word holding blocks
+// 4 g + 0, 4 g + 2, 4 g + 1, 4 g + 3 in bytes 0..3, stored group-major --
+// word (g, row) at g * rows + row -- the layout the MXFP8 GEMM loads whole
+// per K stage (each half of the word is what one half of an MFMA's lanes
+// needs).
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
                                                           int64_t rows, int64_t cols, int64_t ld,
                                                           uint8_t* __restrict__ q,
@@ -309,8 +311,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
             // the codes of the group's other 3 blocks (lanes +4, +8, +12 of the
             // 16-lane DPP row) into the group's first lane
             const uint32_t word = (uint32_t)code |
-                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 8) |
-                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 16) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
             if (idx < nchunk) {
                 const uint4 w = v[u];

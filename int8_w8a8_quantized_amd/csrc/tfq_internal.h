@@ -22,7 +22,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 // MXFP8 rows: E4M3FN codes [rows, cols] and E8M0 scales [rows, cols / 32]
 // (cols % 32 == 0).
 // MXFP8 rows (cols % 128 == 0): codes [rows, cols], E8M0 scale words
-// [cols/128, rows] (byte j of word (g, r) = block 4 g + j of row r)
+// [cols/128, rows] (bytes 0..3 of word (g, r) = blocks 4 g + 0, 2, 1, 3 of
+// row r)
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* q, uint32_t* scale, hipStream_t stream);
 

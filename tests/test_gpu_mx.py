@@ -8,7 +8,8 @@ oracle's binary64 sum over the same quantised operands.  Inputs vary their
 magnitude from one 32-block to the next, so a scale applied to the wrong
 block fails the check.  The oracle keeps scales as [rows, cols/32]; the
 library stores them as [cols/128, rows, 4] (the four block scales of a
-128-wide K group together, group-major): `grouped` and `ungrouped` convert.
+128-wide K group together, in the byte order 0, 2, 1, 3, group-major):
+`grouped` and `ungrouped` convert.
 """
 import numpy as np
 import pytest
@@ -28,16 +29,19 @@ def tfq():
     return m
 
 
+ORDER = [0, 2, 1, 3]  # block (within a group of 4) held by each byte of a scale word
+
+
 def grouped(s):
     """[rows, cols/32] -> [cols/128, rows, 4]."""
     r, nb = s.shape
-    return np.ascontiguousarray(s.reshape(r, nb // 4, 4).transpose(1, 0, 2))
+    return np.ascontiguousarray(s.reshape(r, nb // 4, 4)[:, :, ORDER].transpose(1, 0, 2))
 
 
 def ungrouped(s):
     """[cols/128, rows, 4] -> [rows, cols/32]."""
     g, r, _ = s.shape
-    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(r, 4 * g))
+    return np.ascontiguousarray(s[:, :, ORDER].transpose(1, 0, 2).reshape(r, 4 * g))
 
 
 def _blocky(rng, rows, cols, sigma=1.0, spread=6):
