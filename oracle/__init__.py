@@ -270,6 +270,55 @@ def linear_mx_ref(a_q, a_scale, b_q, b_scale, bias=None, gelu: bool = False, row
     return out
 
 
+# --------------------------------------------------------------------------
+# MoE routed W8A8 -- TeleFuser "Quantization", "Other quantized data paths"
+# (LingBot-Video MoE FP8): expert weights quantised per output channel,
+# the routed activations quantised per row, then one scaled matmul per
+# expert.  Reading: the routed rows of an expert are contiguous (rows
+# offsets[e] .. offsets[e+1]); which token goes to which row is the router's
+# choice, given here as a row index.
+# --------------------------------------------------------------------------
+def gather_rows(x_bf16: np.ndarray, index) -> np.ndarray:
+    """Rows index[r] of x (BF16 bits); an index outside [0, rows) gives a zero row."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    idx = np.asarray(index, dtype=np.int64)
+    out = np.zeros((idx.shape[0], x.shape[1]), dtype=np.uint16)
+    ok = (idx >= 0) & (idx < x.shape[0])
+    out[ok] = x[idx[ok]]
+    return out
+
+
+def quantize_rows_gather(x_bf16: np.ndarray, index, qtype, qmax: float, group: int = 0):
+    """Per-row (or 1x128-group) quantisation of the gathered rows x[index[r]]."""
+    return quantize_rows(gather_rows(x_bf16, index), qtype, qmax, group)
+
+
+def grouped_linear_ref(a_q, a_scale, b_q, b_scale, offsets, qtype="fp8", bias=None,
+                       gelu: bool = False, rows=None) -> np.ndarray:
+    """Routed Linear y [R, N] in binary64: row m of group e (offsets[e] <= m <
+    offsets[e+1]) is the scaled Linear of a[m] against expert e's weights
+    b_q[e] [N, K], b_scale[e] [N] (and bias[e]); rows in no group are NaN.
+    offsets: non-decreasing, offsets[0] >= 0, offsets[-1] <= M."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    b = np.ascontiguousarray(b_q).view(np.uint8)
+    M, K = a.shape
+    E, N, Kb = b.shape
+    assert Kb == K
+    off = np.asarray(offsets, dtype=np.int64)
+    assert off.shape == (E + 1,) and off[0] >= 0 and off[-1] <= M and np.all(np.diff(off) >= 0)
+    sel = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.full((sel.shape[0], N), np.nan)
+    group_of = np.searchsorted(off, sel, side="right") - 1
+    for e in range(E):
+        pick = np.nonzero((group_of == e) & (sel < off[e + 1]))[0]
+        if pick.size == 0:
+            continue
+        out[pick] = linear_ref(a, a_scale, b[e], np.asarray(b_scale)[e], qtype,
+                               bias=None if bias is None else np.asarray(bias)[e], gelu=gelu,
+                               rows=sel[pick])
+    return out
+
+
 def int8_linear(a_q, a_scale, b_q, b_scale, bias=None, rows=None, want_acc=True,
                 want_bf16=True):
     """INT8 W8A8: (acc int64 [R,N] or None, y bf16 bits uint16 [R,N] or None)."""
