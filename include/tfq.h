@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 2
+#define TFQ_ABI_VERSION 3
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -95,6 +95,25 @@ typedef enum tfq_epilogue {
 tfq_status tfq_quantize_rows(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                              int32_t qtype, float qmax, int32_t group_cols, void* q_out,
                              float* scale_out, void* stream);
+
+/*
+ * Routed (gathered) per-token quantisation for a MoE layer: output row r
+ * quantises row row_index[r] of x, exactly as tfq_quantize_rows would.
+ * TeleFuser "Quantization", "Other quantized data paths" (LingBot-Video MoE
+ * FP8: the routed activations are quantised per row); the router's token
+ * order (e.g. tokens sorted by expert, a token repeated once per chosen
+ * expert) is the caller's.
+ *
+ *   x_bf16    [src_rows, cols] BF16, row stride ld_x (as tfq_quantize_rows).
+ *   row_index [rows] int32 device array, 4-byte aligned; an index outside
+ *             [0, src_rows) quantises a row of zeros (codes 0, scale 0).
+ *   q_out [rows, cols], scale_out [rows] or [rows, cols/128]: as
+ *   tfq_quantize_rows.  rows, src_rows >= 1.
+ */
+tfq_status tfq_quantize_rows_gather(const void* x_bf16, int64_t src_rows, int64_t cols,
+                                    int64_t ld_x, const int32_t* row_index, int64_t rows,
+                                    int32_t qtype, float qmax, int32_t group_cols, void* q_out,
+                                    float* scale_out, void* stream);
 
 /*
  * Weight quantisation, one absmax scale per output channel (row of W) or per
@@ -155,6 +174,32 @@ tfq_status tfq_scaled_mm_int8(const int8_t* a_q, const float* a_scale, const int
                               const float* b_scale, int64_t m, int64_t n, int64_t k,
                               const void* bias_bf16, int32_t epi, void* y_bf16, int32_t* acc_i32,
                               void* stream);
+
+/*
+ * Grouped (MoE) scaled FP8 GEMM: rows group_offsets[g] .. group_offsets[g+1]
+ * of a_q are multiplied by expert g's weights, y[m,:] = the scaled product
+ * of a_q[m] with b_q[g] as in tfq_scaled_mm_fp8 (per-row a_scale, per-output-
+ * channel b_scale[g], optional bias[g], epilogue).  TeleFuser "Quantization",
+ * "Other quantized data paths" (LingBot-Video MoE FP8: expert weights per
+ * output channel, routed activations per row, a scaled matmul per expert).
+ *
+ *   a_q [m, k] E4M3FN codes, a_scale [m] (e.g. from
+ *   tfq_quantize_rows_gather, rows sorted by expert).
+ *   b_q [groups, n, k] codes, b_scale [groups, n] FP32, bias_bf16
+ *   [groups, n] BF16 or NULL.
+ *   group_offsets [groups + 1] int32 DEVICE array, 4-byte aligned, read by
+ *   the kernel: non-decreasing, group_offsets[0] >= 0, group_offsets[groups]
+ *   <= m.  Rows in no group are not written.  Offsets that break these rules
+ *   are clamped to [0, m] (every access stays in bounds) but give unspecified
+ *   results.
+ *   y_bf16 [m, n] BF16, 16-byte aligned.
+ *   1 <= groups <= 256; m >= 1; n >= 8, n % 8 == 0; 16 <= k <= 4194304,
+ *   k % 16 == 0.
+ */
+tfq_status tfq_grouped_scaled_mm_fp8(const uint8_t* a_q, const float* a_scale, const uint8_t* b_q,
+                                     const float* b_scale, const int32_t* group_offsets,
+                                     int32_t groups, int64_t m, int64_t n, int64_t k,
+                                     const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
 
 /*
  * Bytes of workspace tfq_quant_linear_fused needs: the activation codes

@@ -23,6 +23,7 @@ __all__ = [
     "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
     "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
+    "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8",
     "tfq_abi_version", "QuantLinear",
 ]
 
@@ -77,6 +78,27 @@ def tfq_quantize_rows(x: torch.Tensor, qtype="fp8", qmax: float = 448.0, group_c
     return q_out, scale_out
 
 
+def tfq_quantize_rows_gather(x: torch.Tensor, row_index: torch.Tensor, qtype="fp8",
+                             qmax: float = 448.0, group_cols: int = 0, q_out=None, scale_out=None,
+                             stream=None):
+    """Routed per-token quantisation: output row r quantises x[row_index[r]]
+    (row_index int32 on the device; an index outside x's rows gives a zero
+    row).  Returns (codes [rows, cols], scales [rows] or [rows, cols/128])."""
+    qt = _qt(qtype)
+    src_rows, cols = x.shape
+    rows = row_index.shape[0]
+    if q_out is None:
+        q_out = torch.empty((rows, cols), dtype=_code_dtype(qt), device=x.device)
+    if scale_out is None:
+        shape = (rows,) if group_cols == 0 else (rows, cols // max(group_cols, 1))
+        scale_out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    check(lib().tfq_quantize_rows_gather(_ptr(x), src_rows, cols, x.stride(0), _ptr(row_index),
+                                         rows, qt, float(qmax), int(group_cols), _ptr(q_out),
+                                         _ptr(scale_out), _stream(stream)),
+          "tfq_quantize_rows_gather")
+    return q_out, scale_out
+
+
 def tfq_quantize_weight_per_channel(w: torch.Tensor, qtype="fp8", qmax: float = 448.0,
                                     block: int = 0, q_out=None, scale_out=None, stream=None):
     """Weights W [n, k] BF16 -> (codes [n, k], scales [n] or [n/128, k/128])."""
@@ -119,6 +141,22 @@ def tfq_scaled_mm_int8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, want_y: 
                                    _ptr(bias), _epi(epi), _ptr(y), _ptr(acc), _stream(stream)),
           "tfq_scaled_mm_int8")
     return y, acc
+
+
+def tfq_grouped_scaled_mm_fp8(a_q, a_scale, b_q, b_scale, group_offsets, bias=None, epi=None,
+                              y=None, stream=None):
+    """Grouped (MoE) FP8 GEMM: rows group_offsets[g]..group_offsets[g+1] of
+    a_q [m, k] against expert g's b_q[g] [n, k]; group_offsets int32 on the
+    device.  Returns y [m, n] BF16 (rows in no group are left as allocated)."""
+    m, k = a_q.shape
+    groups, n, _ = b_q.shape
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    check(lib().tfq_grouped_scaled_mm_fp8(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale),
+                                          _ptr(group_offsets), groups, m, n, k, _ptr(bias),
+                                          _epi(epi), _ptr(y), _stream(stream)),
+          "tfq_grouped_scaled_mm_fp8")
+    return y
 
 
 def tfq_quant_linear_workspace_bytes(m: int, k: int, qtype="fp8", scale_block: int = 0) -> int:

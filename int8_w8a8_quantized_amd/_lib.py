@@ -31,7 +31,11 @@ _I32 = ctypes.c_int32
 _F = ctypes.c_float
 SIGNATURES = [
     ("tfq_quantize_rows", _I32, [_P, _I64, _I64, _I64, _I32, _F, _I32, _P, _P, _P]),
+    ("tfq_quantize_rows_gather", _I32, [_P, _I64, _I64, _I64, _P, _I64, _I32, _F, _I32, _P, _P,
+                                         _P]),
     ("tfq_quantize_weight_per_channel", _I32, [_P, _I64, _I64, _I32, _F, _I32, _P, _P, _P]),
+    ("tfq_grouped_scaled_mm_fp8", _I32, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P,
+                                         _P]),
     ("tfq_scaled_mm_fp8", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _I32, _P, _P]),
     ("tfq_scaled_mm_int8", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
     ("tfq_quant_linear_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I32, _I32]),

@@ -181,6 +181,34 @@ tfq_status tfq_quantize_rows(const void* x_bf16, int64_t rows, int64_t cols, int
                                                 (hipStream_t)stream));
 }
 
+tfq_status tfq_quantize_rows_gather(const void* x_bf16, int64_t src_rows, int64_t cols,
+                                    int64_t ld_x, const int32_t* row_index, int64_t rows,
+                                    int32_t qtype, float qmax, int32_t group_cols, void* q_out,
+                                    float* scale_out, void* stream)
+{
+    if (!x_bf16 || !row_index || !q_out || !scale_out) return TFQ_ERR_NULL_POINTER;
+    if (!qtype_ok(qtype) || (group_cols != 0 && group_cols != 128)) return TFQ_ERR_UNSUPPORTED;
+    if (rows < 1 || rows > kMaxDim || src_rows < 1 || src_rows > kMaxDim || cols < 16 ||
+        cols > kMaxDim || cols % 16 != 0 || ld_x < cols || ld_x > kMaxDim ||
+        (group_cols == 128 && cols % 128 != 0))
+        return TFQ_ERR_BAD_SHAPE;
+    if (ld_x % 8 != 0 || !aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(scale_out, 4) ||
+        !aligned(row_index, 4))
+        return TFQ_ERR_MISALIGNED;
+    if (!qmax_ok(qtype, qmax)) return TFQ_ERR_BAD_QMAX;
+    const int64_t ng = group_cols == 128 ? cols / 128 : 1;
+    const Range rx = range_of(x_bf16, ((src_rows - 1) * ld_x + cols) * 2);
+    const Range ri = range_of(row_index, rows * 4);
+    const Range rq = range_of(q_out, rows * cols), rs = range_of(scale_out, rows * ng * 4);
+    if (overlap(rq, rs) || overlap(rq, rx) || overlap(rq, ri) || overlap(rs, rx) || overlap(rs, ri))
+        return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    return hip_status(tfq::launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, ld_x, qtype,
+                                                qmax, group_cols, (uint8_t*)q_out, scale_out,
+                                                (hipStream_t)stream, row_index, src_rows));
+}
+
 tfq_status tfq_quantize_weight_per_channel(const void* w_bf16, int64_t n, int64_t k, int32_t qtype,
                                            float qmax, int32_t block, void* q_out,
                                            float* scale_out, void* stream)
@@ -231,6 +259,36 @@ tfq_status tfq_scaled_mm_int8(const int8_t* a_q, const float* a_scale, const int
     tfq::GemmArgs g{(const uint8_t*)a_q, (const uint8_t*)b_q, a_scale, b_scale,
                     (const uint16_t*)bias_bf16, (uint16_t*)y_bf16, acc_i32, m, n, k, tfq::kInt8, 0,
                     epi};
+    return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
+}
+
+tfq_status tfq_grouped_scaled_mm_fp8(const uint8_t* a_q, const float* a_scale, const uint8_t* b_q,
+                                     const float* b_scale, const int32_t* group_offsets,
+                                     int32_t groups, int64_t m, int64_t n, int64_t k,
+                                     const void* bias_bf16, int32_t epi, void* y_bf16, void* stream)
+{
+    if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y_bf16)
+        return TFQ_ERR_NULL_POINTER;
+    if (!epi_ok(epi)) return TFQ_ERR_UNSUPPORTED;
+    if (groups < 1 || groups > 256 || m < 1 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 ||
+        k < 16 || k > ((int64_t)1 << 22) || k % 16 != 0)
+        return TFQ_ERR_BAD_SHAPE;
+    if (((m + 255) / 256 + groups) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
+        !aligned(group_offsets, 4) || (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        return TFQ_ERR_MISALIGNED;
+    const Range ry = range_of(y_bf16, m * n * 2);
+    const Range ins[6] = {range_of(a_q, m * k), range_of(b_q, groups * n * k),
+                          range_of(a_scale, m * 4), range_of(b_scale, groups * n * 4),
+                          range_of(bias_bf16, bias_bf16 ? groups * n * 2 : 0),
+                          range_of(group_offsets, (groups + 1) * 4)};
+    for (const Range& r : ins)
+        if (overlap(r, ry)) return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    tfq::GemmArgs g{a_q, b_q, a_scale, b_scale, (const uint16_t*)bias_bf16, (uint16_t*)y_bf16,
+                    nullptr, m, n, k, tfq::kE4M3FN, 0, epi, nullptr, nullptr, group_offsets,
+                    groups};
     return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
 }
 

@@ -60,7 +60,9 @@ struct Params {
     int32_t* acc;
     int m, n, k;
     int tiles_m, tiles_n;
-    int group_m;  // tile rows per band of the tile order
+    int group_m;           // tile rows per band of the tile order
+    const int32_t* goff;   // grouped (MoE) mode: row offsets [groups + 1]
+    int groups;            // grouped mode: number of weight groups (<= 256)
 };
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
@@ -203,7 +205,7 @@ struct PipeAcc<kMxE4M3> {
     typedef v16f type;
 };
 
-template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_pipe_kernel(const Params p)
 {
@@ -211,13 +213,61 @@ void gemm_pipe_kernel(const Params p)
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    int tm, tn;
-    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    int tm, tn, m0, m_end = p.m;
+    const uint8_t* b_grp = p.b;
+    const float* sb_grp = p.sb;
+    const uint16_t* bias_grp = p.bias;
+    if constexpr (GROUPED) {
+        // Routed (MoE) rows (TeleFuser "Quantization", "Other quantized data
+        // paths": routed activations per row, expert weights per output
+        // channel): group g owns rows goff[g] .. goff[g+1] and weight matrix
+        // g, and takes ceil(rows / 256) tile rows of the tile order.  Thread
+        // g reads its group's offsets, clamped to [0, m] so that any offsets
+        // keep every access in bounds; an inclusive scan over the threads
+        // gives each group's last tile row + 1.
+        int* gs = reinterpret_cast<int*>(smem + PMXS);
+        if (t == 0) gs[256] = gs[257] = gs[258] = 0;  // (kept only if no group matches)
+        int lo = 0, hi = 0, cnt = 0;
+        if (t < p.groups) {
+            lo = min(max(p.goff[t], 0), p.m);
+            hi = max(lo, min(max(p.goff[t + 1], 0), p.m));
+            cnt = (hi - lo + BM - 1) / BM;
+        }
+        int v = cnt;
+        gs[t] = v;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int add = t >= d ? gs[t - d] : 0;
+            __syncthreads();
+            v += add;
+            gs[t] = v;
+            __syncthreads();
+        }
+        // tiles_m bounds the grid; only overlapping (invalid) offsets exceed it
+        const int total = min(gs[255], p.tiles_m);
+        if ((int64_t)blockIdx.x >= (int64_t)total * p.tiles_n) return;
+        map_tile(blockIdx.x, total, p.tiles_n, p.group_m, tm, tn);
+        if (t < p.groups && v - cnt <= tm && tm < v) {
+            gs[256] = t;
+            gs[257] = lo + (tm - (v - cnt)) * BM;
+            gs[258] = hi;
+        }
+        __syncthreads();
+        const int g = gs[256];
+        m0 = gs[257];
+        m_end = gs[258];
+        b_grp += (int64_t)g * p.n * p.k;
+        sb_grp += (int64_t)g * p.n;
+        if (bias_grp != nullptr) bias_grp += (int64_t)g * p.n;
+    } else {
+        map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        m0 = tm * BM;
+    }
+    const int n0 = tn * BN;
     const int K = p.k;
-    const int rows_a = min(BM, p.m - m0), rows_b = min(BN, p.n - n0);
+    const int rows_a = min(BM, m_end - m0), rows_b = min(BN, p.n - n0);
     const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
-    const v4i rb = buffer_rsrc(p.b + (int64_t)n0 * K, rows_b * K);
+    const v4i rb = buffer_rsrc(b_grp + (int64_t)n0 * K, rows_b * K);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     // LDS rows are 128 bytes (one stage of K); the 16-byte chunk index is
@@ -368,9 +418,9 @@ void gemm_pipe_kernel(const Params p)
     if (wave_u == 0 && !MX) {
         lds_dma16(buffer_rsrc(p.sa + m0, rows_a * 4), lane * 16, lds_base + PSCL);
     } else if (wave_u == 1 && !MX) {
-        lds_dma16(buffer_rsrc(p.sb + n0, rows_b * 4), lane * 16, lds_base + PSCL + 1024);
-    } else if (wave_u == 2 && p.bias != nullptr) {
-        lds_dma16(buffer_rsrc(p.bias + n0, rows_b * 2), lane * 16, lds_base + PSCL + 2048);
+        lds_dma16(buffer_rsrc(sb_grp + n0, rows_b * 4), lane * 16, lds_base + PSCL + 1024);
+    } else if (wave_u == 2 && bias_grp != nullptr) {
+        lds_dma16(buffer_rsrc(bias_grp + n0, rows_b * 2), lane * 16, lds_base + PSCL + 2048);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -446,7 +496,7 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int row = m0 + wm * 128 + mi * 32 + fr;
-            if (row >= p.m) continue;
+            if (row >= m_end) continue;
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -471,7 +521,7 @@ void gemm_pipe_kernel(const Params p)
         // waits for the staging writes issued before it).  Bias is always
         // added: without one it is -0.0, which leaves every value (signed
         // zeros, infinities and NaNs included) unchanged.
-        const bool has_bias = p.bias != nullptr;
+        const bool has_bias = bias_grp != nullptr;
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             v4f sc[4];
@@ -515,7 +565,7 @@ void gemm_pipe_kernel(const Params p)
             const int lrow = j * 4 + (lane >> 4);
             const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * EPITCH + ch * 16);
             const int grow = m0 + wm * 128 + lrow;
-            if (grow < p.m && gcol < p.n)
+            if (grow < m_end && gcol < p.n)
                 *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
         }
     }
@@ -979,12 +1029,12 @@ hipError_t launch_block(Params p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int QT, int EPI, bool WANT_Y, bool WANT_ACC>
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
 hipError_t launch_pipe(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC>), dim3(grid), dim3(256), 0, st,
-                       p);
+    hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC, GROUPED>), dim3(grid), dim3(256),
+                       0, st, p);
     return hipGetLastError();
 }
 
@@ -1021,6 +1071,14 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
     p.group_m = band_rows(g.m, g.n, g.k);
+    p.goff = g.group_offsets;
+    p.groups = g.groups;
+    if (g.groups > 0) {
+        // grouped (MoE) FP8: at most ceil(m / 256) + groups tile rows
+        p.tiles_m += g.groups;
+        return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false, true>(p, stream)
+                          : launch_pipe<kE4M3FN, 0, true, false, true>(p, stream);
+    }
     if (g.scale_block == 128)
         return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
     // MXFP8 always takes the 256x256 kernel (its scale ring lives there)

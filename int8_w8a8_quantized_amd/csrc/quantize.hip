@@ -124,17 +124,33 @@ __device__ __forceinline__ uint2 encode_chunk(const uint4& v, const Quotient& d,
 
 constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
 
+// Source of output row `row`: the row itself, or row gather[row] of x for a
+// routed quantisation (TeleFuser "Quantization", "Other quantized data
+// paths": MoE activations are quantised per row after routing).  An index
+// outside [0, src_rows) reads as a row of zeros (ok = false: every load of
+// the row is masked).
+__device__ __forceinline__ const uint4* source_row(const uint16_t* x, int64_t row, int64_t ld,
+                                                  const int32_t* gather, int64_t src_rows,
+                                                  bool& ok)
+{
+    const int64_t r = gather != nullptr ? (int64_t)gather[row] : row;
+    ok = r >= 0 && r < src_rows;
+    return reinterpret_cast<const uint4*>(x + (ok ? r : 0) * ld);
+}
+
 // Per-row quantisation with the row resident in registers (cols <= CH*512).
 template <int QT, int CH>
 __global__ __launch_bounds__(256) void quantize_rows_resident(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-    uint8_t* __restrict__ q, float* __restrict__ scale)
+    uint8_t* __restrict__ q, float* __restrict__ scale, const int32_t* __restrict__ gather,
+    int64_t src_rows)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
-    const int nchunk = (int)(cols >> 3);
+    bool ok;
+    const uint4* xr = source_row(x, row, ld, gather, src_rows, ok);
+    const int nchunk = ok ? (int)(cols >> 3) : 0;
     uint4 v[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -151,10 +167,11 @@ __global__ __launch_bounds__(256) void quantize_rows_resident(
     if (lane == 0) scale[row] = s;
     const Quotient d(s);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    const int nout = (int)(cols >> 3);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = c * 64 + lane;
-        if (idx < nchunk) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
+        if (idx < nout) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
     }
 }
 
@@ -166,20 +183,23 @@ __global__ __launch_bounds__(256) void quantize_rows_resident(
 template <int QT, int CH, int WPR>
 __global__ __launch_bounds__(256) void quantize_rows_split(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-    uint8_t* __restrict__ q, float* __restrict__ scale)
+    uint8_t* __restrict__ q, float* __restrict__ scale, const int32_t* __restrict__ gather,
+    int64_t src_rows)
 {
     __shared__ uint32_t part_max[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int part = wave % WPR;
     const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
     const bool valid = row < rows;  // every wave reaches the barrier
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (valid ? row : 0) * ld);
+    bool ok = false;
+    const uint4* xr = valid ? source_row(x, row, ld, gather, src_rows, ok)
+                            : reinterpret_cast<const uint4*>(x);
     const int nchunk = (int)(cols >> 3);
     uint4 v[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = (part * CH + c) * 64 + lane;
-        v[c] = (valid && idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        v[c] = (ok && idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t m = 0;
 #pragma unroll
@@ -208,22 +228,26 @@ __global__ __launch_bounds__(256) void quantize_rows_split(
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_rows_two_pass(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-    uint8_t* __restrict__ q, float* __restrict__ scale)
+    uint8_t* __restrict__ q, float* __restrict__ scale, const int32_t* __restrict__ gather,
+    int64_t src_rows)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    bool ok;
+    const uint4* xr = source_row(x, row, ld, gather, src_rows, ok);
     const int64_t nchunk = cols >> 3;
     uint32_t m = 0;
-    for (int64_t idx = lane; idx < nchunk; idx += 64) m = abs_max_chunk(m, xr[idx]);
+    if (ok)
+        for (int64_t idx = lane; idx < nchunk; idx += 64) m = abs_max_chunk(m, xr[idx]);
     m = max(m & 0xFFFFu, m >> 16);
     const float amax = __uint_as_float(wave_max(m) << 16);
     const float s = amax / qmax;
     if (lane == 0) scale[row] = s;
     const Quotient d(s);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
-    for (int64_t idx = lane; idx < nchunk; idx += 64) qr[idx] = encode_chunk<QT>(xr[idx], d, qmax);
+    for (int64_t idx = lane; idx < nchunk; idx += 64)
+        qr[idx] = encode_chunk<QT>(ok ? xr[idx] : make_uint4(0u, 0u, 0u, 0u), d, qmax);
 }
 
 // 1x128 groups: 16 lanes x 8 elements cover one group, so every chunk of a
@@ -231,12 +255,14 @@ __global__ __launch_bounds__(256) void quantize_rows_two_pass(
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_groups128(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-    uint8_t* __restrict__ q, float* __restrict__ scale)
+    uint8_t* __restrict__ q, float* __restrict__ scale, const int32_t* __restrict__ gather,
+    int64_t src_rows)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
+    bool ok;
+    const uint4* xr = source_row(x, row, ld, gather, src_rows, ok);
     const int nchunk = (int)(cols >> 3);  // multiple of 16
     const int ngroups = (int)(cols >> 7);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
@@ -247,7 +273,7 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = base + u * 64 + lane;
-            v[u] = (idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = (ok && idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -374,50 +400,57 @@ __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float4* __rest
     q[i] = encode4<kE4M3FN>(v.x, v.y, v.z, v.w, 448.0f);
 }
 
+// source rows of a launch: an optional gather index and the number of rows
+// of x it may name
+struct Src {
+    const int32_t* gather;
+    int64_t rows;
+};
+
 template <int QT, int CH>
 hipError_t launch_resident(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-                           uint8_t* q, float* s, hipStream_t st)
+                           uint8_t* q, float* s, Src src, hipStream_t st)
 {
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL((quantize_rows_resident<QT, CH>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       x, rows, cols, ld, qmax, q, s);
+                       x, rows, cols, ld, qmax, q, s, src.gather, src.rows);
     return hipGetLastError();
 }
 
 template <int QT, int CH, int WPR>
 hipError_t launch_split(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-                        uint8_t* q, float* s, hipStream_t st)
+                        uint8_t* q, float* s, Src src, hipStream_t st)
 {
     const int64_t rpb = 4 / WPR;
     const int64_t blocks = (rows + rpb - 1) / rpb;
     hipLaunchKernelGGL((quantize_rows_split<QT, CH, WPR>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       x, rows, cols, ld, qmax, q, s);
+                       x, rows, cols, ld, qmax, q, s, src.gather, src.rows);
     return hipGetLastError();
 }
 
 template <int QT>
 hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-                          uint8_t* q, float* s, hipStream_t st)
+                          uint8_t* q, float* s, Src src, hipStream_t st)
 {
     const int64_t chunks = (cols >> 3);
     const int64_t per_lane = (chunks + 63) / 64;
-    if (per_lane <= 2) return launch_resident<QT, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 4) return launch_resident<QT, 4>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 6) return launch_resident<QT, 6>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 8) return launch_resident<QT, 8>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 10) return launch_resident<QT, 10>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 12) return launch_resident<QT, 12>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 2) return launch_resident<QT, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 4) return launch_resident<QT, 4>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 6) return launch_resident<QT, 6>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 8) return launch_resident<QT, 8>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 10) return launch_resident<QT, 10>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 12) return launch_resident<QT, 12>(x, rows, cols, ld, qmax, q, s, src, st);
     // longer rows: 2 waves per row up to 16384 columns, 4 up to 32768
-    if (per_lane <= 16) return launch_split<QT, 8, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 20) return launch_split<QT, 10, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 24) return launch_split<QT, 12, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 28) return launch_split<QT, 14, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 32) return launch_split<QT, 16, 2>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 48) return launch_split<QT, 12, 4>(x, rows, cols, ld, qmax, q, s, st);
-    if (per_lane <= 64) return launch_split<QT, 16, 4>(x, rows, cols, ld, qmax, q, s, st);
+    if (per_lane <= 16) return launch_split<QT, 8, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 20) return launch_split<QT, 10, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 24) return launch_split<QT, 12, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 28) return launch_split<QT, 14, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 32) return launch_split<QT, 16, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 48) return launch_split<QT, 12, 4>(x, rows, cols, ld, qmax, q, s, src, st);
+    if (per_lane <= 64) return launch_split<QT, 16, 4>(x, rows, cols, ld, qmax, q, s, src, st);
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL((quantize_rows_two_pass<QT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
-                       rows, cols, ld, qmax, q, s);
+                       rows, cols, ld, qmax, q, s, src.gather, src.rows);
     return hipGetLastError();
 }
 
@@ -425,20 +458,21 @@ hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                 int qtype, float qmax, int group_cols, uint8_t* q, float* scale,
-                                hipStream_t stream)
+                                hipStream_t stream, const int32_t* gather, int64_t src_rows)
 {
+    const Src src{gather, gather != nullptr ? src_rows : rows};
     if (group_cols == 128) {
         const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
         if (qtype == kE4M3FN)
             hipLaunchKernelGGL((quantize_groups128<kE4M3FN>), dim3((unsigned)blocks), dim3(256), 0,
-                               stream, x, rows, cols, ld, qmax, q, scale);
+                               stream, x, rows, cols, ld, qmax, q, scale, src.gather, src.rows);
         else
             hipLaunchKernelGGL((quantize_groups128<kInt8>), dim3((unsigned)blocks), dim3(256), 0,
-                               stream, x, rows, cols, ld, qmax, q, scale);
+                               stream, x, rows, cols, ld, qmax, q, scale, src.gather, src.rows);
         return hipGetLastError();
     }
-    if (qtype == kE4M3FN) return launch_rows_qt<kE4M3FN>(x, rows, cols, ld, qmax, q, scale, stream);
-    return launch_rows_qt<kInt8>(x, rows, cols, ld, qmax, q, scale, stream);
+    if (qtype == kE4M3FN) return launch_rows_qt<kE4M3FN>(x, rows, cols, ld, qmax, q, scale, src, stream);
+    return launch_rows_qt<kInt8>(x, rows, cols, ld, qmax, q, scale, src, stream);
 }
 
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

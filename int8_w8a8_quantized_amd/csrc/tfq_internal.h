@@ -15,12 +15,13 @@ enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2 };
 // assume the arguments already passed the host-side validation.
 
 // Row-wise (group_cols == 0) or 1x128-group (group_cols == 128) quantisation.
+// With `gather`, output row r quantises row gather[r] of x (x has src_rows
+// rows; an index outside [0, src_rows) reads as a zero row).
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                 int qtype, float qmax, int group_cols, uint8_t* q, float* scale,
-                                hipStream_t stream);
+                                hipStream_t stream, const int32_t* gather = nullptr,
+                                int64_t src_rows = 0);
 
-// MXFP8 rows: E4M3FN codes [rows, cols] and E8M0 scales [rows, cols / 32]
-// (cols % 32 == 0).
 // MXFP8 rows (cols % 128 == 0): codes [rows, cols], E8M0 scale words
 // [cols/128, rows] (bytes 0..3 of word (g, r) = blocks 4 g + 0, 2, 1, 3 of
 // row r)
@@ -48,6 +49,10 @@ struct GemmArgs {
     int epi;               // 0 none, 1 gelu-tanh
     const uint32_t* ea;    // MXFP8: E8M0 scale words [k/128, m] (sa, sb unused), else null
     const uint32_t* eb;    // MXFP8: E8M0 scale words [k/128, n], else null
+    // grouped (MoE) FP8: b [groups, n, k], sb [groups, n], bias [groups, n];
+    // rows group_offsets[g] .. group_offsets[g+1] (device int32) use group g
+    const int32_t* group_offsets;
+    int groups;            // 0 = not grouped
 };
 
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);

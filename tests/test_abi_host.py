@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 2
+    assert L.tfq_abi_version() == 3
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -138,6 +138,30 @@ def test_mx_validation(L):
 
 
 @no_gpu_only
+def test_moe_validation(L):
+    q = L.tfq_quantize_rows_gather
+    assert q(A, 10, 64, 64, None, 4, 0, 448.0, 0, B, C, None) == NULL
+    assert q(A, 0, 64, 64, D, 4, 0, 448.0, 0, B, C, None) == SHAPE     # src_rows
+    assert q(A, 10, 64, 64, D, 0, 0, 448.0, 0, B, C, None) == SHAPE     # rows
+    assert q(A, 10, 60, 64, D, 4, 0, 448.0, 0, B, C, None) == SHAPE     # cols % 16
+    assert q(A, 10, 64, 64, D + 2, 4, 0, 448.0, 0, B, C, None) == ALIGN  # index alignment
+    assert q(A, 10, 64, 64, D, 4, 0, 449.0, 0, B, C, None) == QMAX
+    assert q(A, 10, 64, 64, B + 64, 4, 0, 448.0, 0, B, C, None) == ALIAS  # index over codes
+    assert q(A, 10, 64, 64, D, 4, 0, 448.0, 0, A + 640, C, None) == ALIAS  # codes over x row 5
+    g = L.tfq_grouped_scaled_mm_fp8
+    assert g(A, B, C, D, None, 4, 64, 64, 64, None, 0, E, None) == NULL
+    assert g(A, B, C, D, F, 0, 64, 64, 64, None, 0, E, None) == SHAPE    # groups
+    assert g(A, B, C, D, F, 257, 64, 64, 64, None, 0, E, None) == SHAPE
+    assert g(A, B, C, D, F, 4, 64, 60, 64, None, 0, E, None) == SHAPE    # n % 8
+    assert g(A, B, C, D, F, 4, 64, 64, 40, None, 0, E, None) == SHAPE    # k % 16
+    assert g(A, B, C, D, F, 4, 64, 64, 64, None, 3, E, None) == UNSUP    # epilogue
+    assert g(A, B, C, D, F + 2, 4, 64, 64, 64, None, 0, E, None) == ALIGN
+    assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, E + 8, None) == ALIGN
+    assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, F, None) == ALIAS    # y over offsets
+    assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, C + 3 * 64 * 64, None) == ALIAS  # y over b_q[3]
+
+
+@no_gpu_only
 def test_fused_validation(L):
     ws = L.tfq_quant_linear_workspace_bytes
     need = ws(100, 256, 0, 0)
@@ -161,6 +185,13 @@ def test_valid_call_without_gpu_reports_device(L):
     assert L.tfq_e4m3fn_encode_f32(A, B, 64, None) == DEV
     assert L.tfq_quantize_mx(A, 4, 128, 128, B, C, None) == DEV
     assert L.tfq_scaled_mm_mxfp8(A, B, C, D, 64, 64, 128, None, 0, E, None) == DEV
+    assert L.tfq_quantize_rows_gather(A, 10, 64, 64, D, 4, 0, 448.0, 0, B, C, None) == DEV
+    # codes placed right after a source matrix that has fewer rows than the
+    # output: adjacent, not overlapping
+    x_end = A + 97 * 1024 * 2
+    assert L.tfq_quantize_rows_gather(A, 97, 1024, 1024, D, 183, 0, 448.0, 0, x_end,
+                                      x_end + 183 * 1024, None) == DEV
+    assert L.tfq_grouped_scaled_mm_fp8(A, B, C, D, F, 4, 64, 64, 64, None, 0, E, None) == DEV
 
 
 def test_python_binding_names_match_abi():
