@@ -203,6 +203,50 @@ def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y):
     return out
 
 
+def moe_layer(torch, tfq, stream):
+    """A routed FFN-up layer at video-DiT size: 75600 tokens, 8 experts of
+    [13824, 5120], top-2 routing with skewed expert loads.  Synthetic and
+    seeded, generated on the GPU (torch generator, seed 0); the routing (a
+    sort by expert) is set up outside the timed calls.  Timed: the gathered
+    per-row quantisation of the 151200 routed rows and the grouped GEMM with
+    the GELU epilogue (median of 20 each)."""
+    log("extras: moe_video_dit_ffn_up (8 experts, top-2)")
+    T, K, N, E, topk = 75600, 5120, 13824, 8, 2
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((T, K), generator=g, device="cuda").to(torch.bfloat16)
+    p = torch.rand(E, generator=g, device="cuda") ** 3 + 0.02  # skewed expert popularity
+    choice = torch.multinomial(p.expand(T, E), topk, replacement=False, generator=g)
+    expert = choice.reshape(-1)
+    order = torch.sort(expert, stable=True).indices
+    row_index = (order // topk).to(torch.int32)
+    loads = torch.bincount(expert, minlength=E)
+    off = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    off[1:] = torch.cumsum(loads, 0).to(torch.int32)
+    M = T * topk
+    wq = torch.empty((E, N, K), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((E, N), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        w = (torch.randn((N, K), generator=g, device="cuda") * 0.015).to(torch.bfloat16)
+        tfq.tfq_quantize_weight_per_channel(w, "fp8", 448.0, 0, wq[e], ws[e])
+        del w
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms_q, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows_gather(
+        x, row_index, "fp8", 448.0, 0, qa, sa))
+    ms_g, _ = time_calls(torch, stream, lambda: tfq.tfq_grouped_scaled_mm_fp8(
+        qa, sa, wq, ws, off, None, "gelu_tanh", y))
+    fl = 2.0 * M * N * K
+    out = {"tokens": T, "experts": E, "topk": topk, "K": K, "N": N,
+           "expert_rows": loads.tolist(),
+           "gather_quantize": {"ms": ms_q, "gbs": (2 * M * K + M * K + 4 * M) / ms_q / 1e6},
+           "grouped_gemm_gelu": {"ms": ms_g, "tflops": fl / ms_g / 1e9,
+                                 "frac_fp8_peak": fl / ms_g / 1e9 / FP8_PEAK_TFLOPS}}
+    del x, wq, ws, qa, sa, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(d, rows_sample: int):
     """The oracle on host cores over a row sample of the same FFN-pair step:
     quantise the sampled X rows, up GEMM + GELU, BF16 round, quantise G rows,
@@ -347,6 +391,7 @@ def main():
         del x, g, qg, y, qx
         torch.cuda.empty_cache()
         ext.update(extras(torch, tfq, synth, stream))
+        ext["moe_video_dit_ffn_up"] = moe_layer(torch, tfq, stream)
 
     cpu = None
     if not args.no_cpu:

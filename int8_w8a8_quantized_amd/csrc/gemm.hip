@@ -221,19 +221,28 @@ void gemm_pipe_kernel(const Params p)
         // Routed (MoE) rows (TeleFuser "Quantization", "Other quantized data
         // paths": routed activations per row, expert weights per output
         // channel): group g owns rows goff[g] .. goff[g+1] and weight matrix
-        // g, and takes ceil(rows / 256) tile rows of the tile order.  Thread
-        // g reads its group's offsets, clamped to [0, m] so that any offsets
-        // keep every access in bounds; an inclusive scan over the threads
-        // gives each group's last tile row + 1.
+        // g; its ceil(rows / 256) x tiles_n tiles run in bands of group_m
+        // tile rows.  Workgroup b runs on XCD b % 8 as that XCD's
+        // (b / 8)-th workgroup.  Each XCD takes its own eighth of every
+        // group's tiles, group after group, so that all XCDs work on the same
+        // experts' weights at a time (they stay in the Infinity Cache) while
+        // each XCD's tiles are neighbours (its L2 shares their panels).
+        // Thread g reads group g's offsets, clamped to [0, m] so that any
+        // offsets keep every access in bounds; a scan over the threads of
+        // the slice sizes finds the group of this workgroup's tile.
         int* gs = reinterpret_cast<int*>(smem + PMXS);
-        if (t == 0) gs[256] = gs[257] = gs[258] = 0;  // (kept only if no group matches)
-        int lo = 0, hi = 0, cnt = 0;
+        if (t == 0) gs[256] = gs[257] = gs[258] = 0;  // (kept only if no tile is found)
+        const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+        int lo = 0, hi = 0, cnt = 0, s0 = 0, sz = 0;
         if (t < p.groups) {
             lo = min(max(p.goff[t], 0), p.m);
             hi = max(lo, min(max(p.goff[t + 1], 0), p.m));
             cnt = (hi - lo + BM - 1) / BM;
+            const int64_t tiles = (int64_t)cnt * p.tiles_n;
+            s0 = (int)(tiles * xcd / 8);
+            sz = (int)(tiles * (xcd + 1) / 8) - s0;
         }
-        int v = cnt;
+        int v = sz;
         gs[t] = v;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {
@@ -243,19 +252,26 @@ void gemm_pipe_kernel(const Params p)
             gs[t] = v;
             __syncthreads();
         }
-        // tiles_m bounds the grid; only overlapping (invalid) offsets exceed it
-        const int total = min(gs[255], p.tiles_m);
-        if ((int64_t)blockIdx.x >= (int64_t)total * p.tiles_n) return;
-        map_tile(blockIdx.x, total, p.tiles_n, p.group_m, tm, tn);
-        if (t < p.groups && v - cnt <= tm && tm < v) {
+        if (t < p.groups && v - sz <= j && j < v) {
+            // tile s0 + (j - start) of group t, in bands of group_m tile rows
+            const int local = s0 + (j - (v - sz));
+            const int band_tiles = p.group_m * p.tiles_n;
+            const int band = local / band_tiles;
+            const int first = band * p.group_m;
+            const int gm = min(cnt - first, p.group_m);
+            const int in = local - band * band_tiles;
             gs[256] = t;
-            gs[257] = lo + (tm - (v - cnt)) * BM;
+            gs[257] = lo + (first + in % gm) * BM;
             gs[258] = hi;
+            gs[259] = in / gm;
         }
         __syncthreads();
+        if (gs[258] == 0) return;  // no tile for this workgroup (uniform)
         const int g = gs[256];
         m0 = gs[257];
         m_end = gs[258];
+        tn = gs[259];
+        tm = 0;
         b_grp += (int64_t)g * p.n * p.k;
         sb_grp += (int64_t)g * p.n;
         if (bias_grp != nullptr) bias_grp += (int64_t)g * p.n;
@@ -1074,10 +1090,18 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.goff = g.group_offsets;
     p.groups = g.groups;
     if (g.groups > 0) {
-        // grouped (MoE) FP8: at most ceil(m / 256) + groups tile rows
+        // grouped (MoE) FP8: at most ceil(m / 256) + groups tile rows; each
+        // XCD's share of a group's tiles rounds up by at most one, so 8 more
+        // workgroups per group (and 8 spare) cover every tile
         p.tiles_m += g.groups;
-        return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false, true>(p, stream)
-                          : launch_pipe<kE4M3FN, 0, true, false, true>(p, stream);
+        const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n + 8 * g.groups + 8);
+        if (g.epi == 1)
+            hipLaunchKernelGGL((gemm_pipe_kernel<kE4M3FN, 1, true, false, true>), dim3(grid),
+                               dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_pipe_kernel<kE4M3FN, 0, true, false, true>), dim3(grid),
+                               dim3(256), 0, stream, p);
+        return hipGetLastError();
     }
     if (g.scale_block == 128)
         return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
