@@ -319,6 +319,61 @@ def grouped_linear_ref(a_q, a_scale, b_q, b_scale, offsets, qtype="fp8", bias=No
     return out
 
 
+# --------------------------------------------------------------------------
+# FP8 KV cache -- TeleFuser "Quantization", "Other quantized data paths"
+# (LiveAct FP8 KV cache): K and V stored as E4M3FN with one FP32 scale per
+# last-dimension vector, dequantised to the attention's dtype on load.
+# Readings: a vector is quantised exactly as a row of the FP8 activation
+# path (absmax / qmax, qmax = 448 by default); dequantisation is the binary32
+# product scale * value, then one conversion (RNE) to the requested type;
+# tokens are written to / read from cache slots named by an index, and an
+# index outside the cache is skipped (store) or reads as zeros (load).
+# --------------------------------------------------------------------------
+KV_DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
+
+
+def kv_store(kv_bf16: np.ndarray, slot, cache: np.ndarray, scale: np.ndarray,
+             qmax: float = 448.0) -> None:
+    """Quantise kv [tokens, heads, head_dim] (BF16 bits) per (token, head)
+    vector into cache [slots, heads, head_dim] (uint8) and scale [slots, heads]
+    (float32) at rows slot[token], in place; out-of-range slots are skipped.
+    Slots must be distinct."""
+    kv = np.ascontiguousarray(kv_bf16, dtype=np.uint16)
+    T, H, D = kv.shape
+    sl = np.asarray(slot, dtype=np.int64)
+    ok = (sl >= 0) & (sl < cache.shape[0])
+    assert np.unique(sl[ok]).size == int(ok.sum()), "distinct slots"
+    if not ok.any():
+        return
+    q, s = quantize_rows(kv[ok].reshape(-1, D), "fp8", qmax)
+    cache[sl[ok]] = q.reshape(-1, H, D)
+    scale[sl[ok]] = s.reshape(-1, H)
+
+
+def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """binary32 -> BF16 bits, round to nearest even (finite values)."""
+    b = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def kv_load(cache: np.ndarray, scale: np.ndarray, index, out_dtype: str = "bf16") -> np.ndarray:
+    """Dequantised rows index[i] of the cache: [n, heads, head_dim] as BF16
+    bits (uint16), FP16 bits (uint16) or float32; out-of-range rows are zero."""
+    idx = np.asarray(index, dtype=np.int64)
+    S, H, D = cache.shape
+    ok = (idx >= 0) & (idx < S)
+    vals = e4m3fn_table().astype(np.float32)
+    prod = np.zeros((idx.shape[0], H, D), dtype=np.float32)
+    prod[ok] = np.asarray(scale, dtype=np.float32)[idx[ok]][:, :, None] * vals[cache[idx[ok]]]
+    if out_dtype == "fp32":
+        return prod
+    if out_dtype == "bf16":
+        return f32_to_bf16_bits(prod)
+    if out_dtype == "fp16":
+        return prod.astype(np.float16).view(np.uint16)
+    raise ValueError(out_dtype)
+
+
 def int8_linear(a_q, a_scale, b_q, b_scale, bias=None, rows=None, want_acc=True,
                 want_bf16=True):
     """INT8 W8A8: (acc int64 [R,N] or None, y bf16 bits uint16 [R,N] or None)."""
