@@ -247,6 +247,34 @@ def moe_layer(torch, tfq, stream):
     return out
 
 
+def kv_cache(torch, tfq, stream):
+    """FP8 KV cache at video-DiT attention size: K [75600 tokens, 40 heads,
+    128] BF16 stored into a cache (slots in reverse token order) and loaded
+    back to BF16 in a random order; synthetic N(0,1), torch generator seed 0.
+    HBM bytes per call: store 2 + 1 per element + 4 per vector + 4 per token;
+    load 1 + 2 per element + 4 per vector + 4 per token."""
+    log("extras: kv_cache_video_dit (75600 x 40 x 128)")
+    T, H, D = 75600, 40, 128
+    g = torch.Generator(device="cuda").manual_seed(0)
+    kv = torch.randn((T, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    slot = torch.arange(T - 1, -1, -1, dtype=torch.int32, device="cuda")
+    order = torch.randperm(T, generator=g, device="cuda").to(torch.int32)
+    cache = torch.empty((T, H, D), dtype=torch.uint8, device="cuda")
+    scale = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    E = T * H * D
+    ms_s, _ = time_calls(torch, stream, lambda: tfq.tfq_kv_cache_store(kv, slot, cache, scale))
+    ms_l, _ = time_calls(torch, stream, lambda: tfq.tfq_kv_cache_load(cache, scale, order,
+                                                                       out=out))
+    res = {"store": {"ms": ms_s, "gbs": (3 * E + 4 * T * H + 4 * T) / ms_s / 1e6},
+           "load_bf16": {"ms": ms_l, "gbs": (3 * E + 4 * T * H + 4 * T) / ms_l / 1e6}}
+    for k in res:
+        res[k]["frac_hbm"] = res[k]["gbs"] / HBM_PEAK_GBS
+    del kv, cache, scale, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(d, rows_sample: int):
     """The oracle on host cores over a row sample of the same FFN-pair step:
     quantise the sampled X rows, up GEMM + GELU, BF16 round, quantise G rows,
@@ -392,6 +420,7 @@ def main():
         torch.cuda.empty_cache()
         ext.update(extras(torch, tfq, synth, stream))
         ext["moe_video_dit_ffn_up"] = moe_layer(torch, tfq, stream)
+        ext["kv_cache_video_dit"] = kv_cache(torch, tfq, stream)
 
     cpu = None
     if not args.no_cpu:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 3
+#define TFQ_ABI_VERSION 4
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -283,6 +283,42 @@ tfq_status tfq_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64
 tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
                                const uint32_t* b_scale, int64_t m, int64_t n, int64_t k,
                                const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
+
+/*
+ * FP8 KV cache.  TeleFuser "Quantization", "Other quantized data paths"
+ * (LiveAct FP8 KV cache: K/V stored as E4M3FN with one FP32 scale per
+ * last-dimension vector, dequantised to the requested attention dtype on
+ * load).  A cache holds `slots` rows of [heads, head_dim] E4M3FN codes
+ * (uint8 [slots, heads, head_dim], 16-byte aligned) and their scales
+ * (FP32 [slots, heads]); K and V are two such caches.
+ *
+ * Store: each vector kv[t, h, :] is quantised exactly as an FP8 row of
+ * tfq_quantize_rows (s = RN32(amax / qmax), codes E4M3FN_RNE(clamp(RN32(x /
+ * s), ±qmax))) into cache row slot_index[t], head h.
+ *   kv_bf16    [tokens, heads, head_dim] BF16, token stride ld_token elements
+ *              (ld_token >= heads * head_dim, ld_token % 8 == 0), heads
+ *              contiguous, 16-byte aligned.
+ *   slot_index [tokens] int32 DEVICE array; a slot outside [0, slots) is
+ *              not written.  Slots must be distinct (else which token's
+ *              vector a slot keeps is unspecified).
+ *   qmax       E4M3FN grid value <= 448 (448 = the full range).
+ *   8 <= head_dim <= 512, head_dim % 8 == 0.
+ */
+tfq_status tfq_kv_cache_store(const void* kv_bf16, int64_t tokens, int64_t heads, int64_t head_dim,
+                              int64_t ld_token, const int32_t* slot_index, int64_t slots,
+                              float qmax, uint8_t* cache, float* cache_scale, void* stream);
+
+/*
+ * Load (dequantise): out[i, h, :] = cache_scale[j, h] * value(cache[j, h, :])
+ * for j = slot_index[i]: the E4M3FN value is exact, the product one binary32
+ * multiplication (RNE), then one conversion (RNE) to out_dtype: 0 = BF16,
+ * 1 = FP16, 2 = FP32.  A slot outside [0, slots) gives a zero vector.
+ *   slot_index [n] int32 DEVICE array; out [n, heads, head_dim], 16-byte
+ *   aligned.
+ */
+tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int64_t slots,
+                             int64_t heads, int64_t head_dim, const int32_t* slot_index, int64_t n,
+                             int32_t out_dtype, void* out, void* stream);
 
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream);
 

@@ -23,12 +23,14 @@ __all__ = [
     "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
     "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
-    "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8",
+    "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
+    "tfq_kv_cache_load", "KV_DTYPE",
     "tfq_abi_version", "QuantLinear",
 ]
 
 QTYPE = {"fp8": 0, "e4m3fn": 0, "int8": 1}
 EPI = {None: 0, "none": 0, "gelu_tanh": 1, "gelu": 1}
+KV_DTYPE = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 
 def _qt(qtype) -> int:
@@ -210,6 +212,32 @@ def tfq_scaled_mm_mxfp8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None,
                                     _ptr(bias), _epi(epi), _ptr(y), _stream(stream)),
           "tfq_scaled_mm_mxfp8")
     return y
+
+
+def tfq_kv_cache_store(kv: torch.Tensor, slot_index: torch.Tensor, cache: torch.Tensor,
+                       cache_scale: torch.Tensor, qmax: float = 448.0, stream=None):
+    """Quantise kv [tokens, heads, head_dim] BF16 (heads and head_dim
+    contiguous) per vector into cache [slots, heads, head_dim] uint8 and
+    cache_scale [slots, heads] FP32 at rows slot_index[t] (int32, device)."""
+    tokens, heads, hd = kv.shape
+    assert kv.stride(2) == 1 and kv.stride(1) == hd
+    check(lib().tfq_kv_cache_store(_ptr(kv), tokens, heads, hd, kv.stride(0), _ptr(slot_index),
+                                   cache.shape[0], float(qmax), _ptr(cache), _ptr(cache_scale),
+                                   _stream(stream)), "tfq_kv_cache_store")
+
+
+def tfq_kv_cache_load(cache: torch.Tensor, cache_scale: torch.Tensor, slot_index: torch.Tensor,
+                      dtype=torch.bfloat16, out=None, stream=None):
+    """Dequantised cache rows slot_index[i]: [n, heads, head_dim] in dtype
+    (bfloat16, float16 or float32)."""
+    slots, heads, hd = cache.shape
+    n = slot_index.shape[0]
+    if out is None:
+        out = torch.empty((n, heads, hd), dtype=dtype, device=cache.device)
+    check(lib().tfq_kv_cache_load(_ptr(cache), _ptr(cache_scale), slots, heads, hd,
+                                  _ptr(slot_index), n, KV_DTYPE[out.dtype], _ptr(out),
+                                  _stream(stream)), "tfq_kv_cache_load")
+    return out
 
 
 def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):

@@ -387,6 +387,59 @@ tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, cons
     return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
 }
 
+tfq_status tfq_kv_cache_store(const void* kv_bf16, int64_t tokens, int64_t heads, int64_t head_dim,
+                              int64_t ld_token, const int32_t* slot_index, int64_t slots,
+                              float qmax, uint8_t* cache, float* cache_scale, void* stream)
+{
+    if (!kv_bf16 || !slot_index || !cache || !cache_scale) return TFQ_ERR_NULL_POINTER;
+    if (tokens < 1 || tokens > kMaxDim || heads < 1 || heads > 65536 || head_dim < 8 ||
+        head_dim > 512 || head_dim % 8 != 0 || slots < 1 || slots > kMaxDim ||
+        ld_token < heads * head_dim || ld_token > ((int64_t)1 << 40) || tokens * heads > kMaxDim ||
+        slots * heads > kMaxDim)
+        return TFQ_ERR_BAD_SHAPE;
+    if (ld_token % 8 != 0 || !aligned(kv_bf16, 16) || !aligned(cache, 16) ||
+        !aligned(cache_scale, 4) || !aligned(slot_index, 4))
+        return TFQ_ERR_MISALIGNED;
+    if (!qmax_ok(TFQ_QTYPE_E4M3FN, qmax)) return TFQ_ERR_BAD_QMAX;
+    const Range rkv = range_of(kv_bf16, ((tokens - 1) * ld_token + heads * head_dim) * 2);
+    const Range rsl = range_of(slot_index, tokens * 4);
+    const Range rc = range_of(cache, slots * heads * head_dim);
+    const Range rs = range_of(cache_scale, slots * heads * 4);
+    if (overlap(rc, rs) || overlap(rc, rkv) || overlap(rc, rsl) || overlap(rs, rkv) ||
+        overlap(rs, rsl))
+        return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    return hip_status(tfq::launch_kv_store((const uint16_t*)kv_bf16, tokens, (int)heads,
+                                           (int)head_dim, ld_token, slot_index, slots, qmax, cache,
+                                           cache_scale, (hipStream_t)stream));
+}
+
+tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int64_t slots,
+                             int64_t heads, int64_t head_dim, const int32_t* slot_index, int64_t n,
+                             int32_t out_dtype, void* out, void* stream)
+{
+    if (!cache || !cache_scale || !slot_index || !out) return TFQ_ERR_NULL_POINTER;
+    if (out_dtype < 0 || out_dtype > 2) return TFQ_ERR_UNSUPPORTED;
+    if (n < 1 || n > kMaxDim || heads < 1 || heads > 65536 || head_dim < 8 || head_dim > 512 ||
+        head_dim % 8 != 0 || slots < 1 || slots > kMaxDim || n * heads > kMaxDim ||
+        slots * heads > kMaxDim)
+        return TFQ_ERR_BAD_SHAPE;
+    if (!aligned(cache, 16) || !aligned(cache_scale, 4) || !aligned(slot_index, 4) ||
+        !aligned(out, 16))
+        return TFQ_ERR_MISALIGNED;
+    const int64_t esize = out_dtype == 2 ? 4 : 2;
+    const Range ro = range_of(out, n * heads * head_dim * esize);
+    if (overlap(ro, range_of(cache, slots * heads * head_dim)) ||
+        overlap(ro, range_of(cache_scale, slots * heads * 4)) ||
+        overlap(ro, range_of(slot_index, n * 4)))
+        return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    return hip_status(tfq::launch_kv_load(cache, cache_scale, slots, (int)heads, (int)head_dim,
+                                          slot_index, n, out_dtype, out, (hipStream_t)stream));
+}
+
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream)
 {
     if (!x || !q) return TFQ_ERR_NULL_POINTER;

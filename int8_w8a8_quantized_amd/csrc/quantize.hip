@@ -354,6 +354,98 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
     }
 }
 
+// FP8 KV cache (TeleFuser "Quantization", "Other quantized data paths":
+// LiveAct stores K and V as E4M3FN with one FP32 scale per last-dimension
+// vector and dequantises them to the attention's dtype on load).
+//
+// Store: each (token, head) vector of head_dim elements is quantised as an
+// FP8 activation row (absmax / qmax, the same division and encoding) and
+// written to cache row slot[token] * heads + head.  P lanes (a power of two,
+// 8 elements each, P * 8 >= head_dim) hold one vector, 64 / P vectors per
+// wave; the absmax is combined over the vector's lanes by shuffles.  A slot
+// outside [0, slots) is not written.
+template <int P>
+__global__ __launch_bounds__(256) void kv_store_kernel(
+    const uint16_t* __restrict__ kv, int64_t tokens, int heads, int hd, int64_t ld_token,
+    const int32_t* __restrict__ slot, int64_t slots, float qmax, uint8_t* __restrict__ cache,
+    float* __restrict__ scale)
+{
+    // (tokens * heads <= 2^30: 32-bit vector indices)
+    const int v = (int)blockIdx.x * (256 / P) + (int)threadIdx.x / P;
+    const int li = threadIdx.x % P;
+    const bool in = v < (int)(tokens * heads);
+    const int tok = in ? v / heads : 0;
+    const int h = in ? v - tok * heads : 0;
+    const bool act = in && li < (hd >> 3);
+    const uint4 x = act ? reinterpret_cast<const uint4*>(kv + (int64_t)tok * ld_token + (int64_t)h * hd)[li]
+                        : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t m = abs_max_chunk(0u, x);
+    m = max(m & 0xFFFFu, m >> 16);
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    const float s = __uint_as_float(m << 16) / qmax;  // correctly rounded (IEEE division)
+    const int64_t sl = in ? (int64_t)slot[tok] : -1;
+    if (act && sl >= 0 && sl < slots) {
+        const int64_t row = sl * heads + h;
+        const Quotient d(s);
+        reinterpret_cast<uint2*>(cache + row * hd)[li] = encode_chunk<kE4M3FN>(x, d, qmax);
+        if (li == 0) scale[row] = s;
+    }
+}
+
+// Load: output vector (i, head) = scale * value of cache row
+// index[i] * heads + head -- the E4M3FN decode is exact, the product is one
+// binary32 multiplication (RNE), then one conversion to the output type
+// (RNE).  An index outside [0, slots) gives a zero vector.  P threads (a
+// power of two, 8 elements each) per vector.
+typedef float v2f_q __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_q __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h_q __attribute__((ext_vector_type(2)));
+
+template <int OUT, int P>  // OUT: 0 BF16, 1 FP16, 2 FP32
+__global__ __launch_bounds__(256) void kv_load_kernel(
+    const uint8_t* __restrict__ cache, const float* __restrict__ scale, int64_t slots, int heads,
+    int hd, const int32_t* __restrict__ index, int64_t n, void* __restrict__ out)
+{
+    // (n * heads <= 2^30: 32-bit vector indices)
+    const int vec = (int)blockIdx.x * (256 / P) + (int)threadIdx.x / P;
+    const int ci = threadIdx.x % P;
+    if (vec >= (int)(n * heads) || ci >= (hd >> 3)) return;
+    const int i = vec / heads;
+    const int h = vec - i * heads;
+    const int64_t sl = index[i];
+    v2f_q f[4];
+    if (sl >= 0 && sl < slots) {
+        const int64_t row = sl * heads + h;
+        const uint2 q = reinterpret_cast<const uint2*>(cache + row * hd)[ci];
+        const float s = scale[row];
+        f[0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false) * s;
+        f[1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true) * s;
+        f[2] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false) * s;
+        f[3] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true) * s;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = v2f_q{0.0f, 0.0f};
+    }
+    const int64_t e0 = (int64_t)vec * hd + ci * 8;
+    if constexpr (OUT == 2) {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+        o[0] = make_float4(f[0].x, f[0].y, f[1].x, f[1].y);
+        o[1] = make_float4(f[2].x, f[2].y, f[3].x, f[3].y);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (OUT == 0)
+                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2bf_q));
+            else
+                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2h_q));
+        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // 128x128 weight blocks: one workgroup (256 threads) per block.
 template <int QT>
 __global__ __launch_bounds__(256) void quantize_blocks128(
@@ -494,6 +586,62 @@ hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int q
     else
         hipLaunchKernelGGL((quantize_blocks128<kInt8>), dim3((unsigned)blocks), dim3(256), 0,
                            stream, w, n, k, qmax, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int hd, int64_t ld_token,
+                           const int32_t* slot, int64_t slots, float qmax, uint8_t* cache,
+                           float* scale, hipStream_t stream)
+{
+    const int lanes = (hd + 7) / 8;
+    const int64_t nvec = tokens * heads;
+#define TFQ_KV_STORE(P)                                                                           \
+    hipLaunchKernelGGL((kv_store_kernel<P>), dim3((unsigned)((nvec + 256 / P - 1) / (256 / P))),   \
+                       dim3(256), 0, stream, kv, tokens, heads, hd, ld_token, slot, slots, qmax,    \
+                       cache, scale)
+    if (lanes <= 4)
+        TFQ_KV_STORE(4);
+    else if (lanes <= 8)
+        TFQ_KV_STORE(8);
+    else if (lanes <= 16)
+        TFQ_KV_STORE(16);
+    else if (lanes <= 32)
+        TFQ_KV_STORE(32);
+    else
+        TFQ_KV_STORE(64);
+#undef TFQ_KV_STORE
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_load(const uint8_t* cache, const float* scale, int64_t slots, int heads, int hd,
+                          const int32_t* index, int64_t n, int out_dtype, void* out,
+                          hipStream_t stream)
+{
+    const int lanes = (hd + 7) / 8;
+    const int64_t nvec = n * heads;
+#define TFQ_KV_LOAD(O, P)                                                                         \
+    hipLaunchKernelGGL((kv_load_kernel<O, P>), dim3((unsigned)((nvec + 256 / P - 1) / (256 / P))), \
+                       dim3(256), 0, stream, cache, scale, slots, heads, hd, index, n, out)
+#define TFQ_KV_LOAD_P(O)       \
+    if (lanes <= 4)            \
+        TFQ_KV_LOAD(O, 4);     \
+    else if (lanes <= 8)       \
+        TFQ_KV_LOAD(O, 8);     \
+    else if (lanes <= 16)      \
+        TFQ_KV_LOAD(O, 16);    \
+    else if (lanes <= 32)      \
+        TFQ_KV_LOAD(O, 32);    \
+    else                       \
+        TFQ_KV_LOAD(O, 64)
+    if (out_dtype == 0) {
+        TFQ_KV_LOAD_P(0);
+    } else if (out_dtype == 1) {
+        TFQ_KV_LOAD_P(1);
+    } else {
+        TFQ_KV_LOAD_P(2);
+    }
+#undef TFQ_KV_LOAD_P
+#undef TFQ_KV_LOAD
     return hipGetLastError();
 }
 

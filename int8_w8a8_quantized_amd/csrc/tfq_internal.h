@@ -28,6 +28,16 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* q, uint32_t* scale, hipStream_t stream);
 
+// FP8 KV cache: store kv [tokens, heads, hd] (token stride ld_token) into
+// cache rows slot[t] * heads + h; load rows index[i] dequantised to
+// out_dtype (0 BF16, 1 FP16, 2 FP32) as [n, heads, hd].
+hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int hd, int64_t ld_token,
+                           const int32_t* slot, int64_t slots, float qmax, uint8_t* cache,
+                           float* scale, hipStream_t stream);
+hipError_t launch_kv_load(const uint8_t* cache, const float* scale, int64_t slots, int heads, int hd,
+                          const int32_t* index, int64_t n, int out_dtype, void* out,
+                          hipStream_t stream);
+
 // 128x128 block weight quantisation (n % 128 == 0, k % 128 == 0).
 hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int qtype, float qmax,
                                   uint8_t* q, float* scale, hipStream_t stream);

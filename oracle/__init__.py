@@ -370,7 +370,8 @@ def kv_load(cache: np.ndarray, scale: np.ndarray, index, out_dtype: str = "bf16"
     if out_dtype == "bf16":
         return f32_to_bf16_bits(prod)
     if out_dtype == "fp16":
-        return prod.astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):  # beyond FP16's range: infinity
+            return prod.astype(np.float16).view(np.uint16)
     raise ValueError(out_dtype)
 
 

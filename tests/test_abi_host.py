@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 3
+    assert L.tfq_abi_version() == 4
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -159,6 +159,33 @@ def test_moe_validation(L):
     assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, E + 8, None) == ALIGN
     assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, F, None) == ALIAS    # y over offsets
     assert g(A, B, C, D, F, 4, 64, 64, 64, None, 0, C + 3 * 64 * 64, None) == ALIAS  # y over b_q[3]
+
+
+@no_gpu_only
+def test_kv_cache_validation(L):
+    st = L.tfq_kv_cache_store
+    #         kv  T  H  D    ld   slot S   qmax   cache scale
+    assert st(A, 4, 2, 128, 256, B, 10, 448.0, C, D, None) == DEV
+    assert st(None, 4, 2, 128, 256, B, 10, 448.0, C, D, None) == NULL
+    assert st(A, 4, 2, 128, 256, None, 10, 448.0, C, D, None) == NULL
+    assert st(A, 4, 2, 120, 240, B, 10, 448.0, C, D, None) == DEV      # head_dim 120 is fine
+    assert st(A, 4, 2, 100, 200, B, 10, 448.0, C, D, None) == SHAPE    # head_dim % 8
+    assert st(A, 4, 2, 520, 1040, B, 10, 448.0, C, D, None) == SHAPE   # head_dim > 512
+    assert st(A, 4, 2, 128, 200, B, 10, 448.0, C, D, None) == SHAPE    # ld < heads * head_dim
+    assert st(A, 4, 2, 128, 260, B, 10, 448.0, C, D, None) == ALIGN    # ld % 8
+    assert st(A, 4, 2, 128, 256, B, 10, 448.0, C + 8, D, None) == ALIGN
+    assert st(A, 4, 2, 128, 256, B + 2, 10, 448.0, C, D, None) == ALIGN
+    assert st(A, 4, 2, 128, 256, B, 10, 500.0, C, D, None) == QMAX
+    assert st(A, 4, 2, 128, 256, B, 10, 448.0, C, C + 2048, None) == ALIAS  # scales inside cache
+    assert st(A, 4, 2, 128, 256, B, 10, 448.0, A + 512, D, None) == ALIAS   # cache over kv
+    ld = L.tfq_kv_cache_load
+    #         cache scale S  H  D   idx n  dtype out
+    assert ld(C, D, 10, 2, 128, B, 4, 0, E, None) == DEV
+    assert ld(C, D, 10, 2, 128, B, 4, 3, E, None) == UNSUP     # dtype
+    assert ld(C, D, 10, 2, 128, None, 4, 0, E, None) == NULL
+    assert ld(C, D, 10, 2, 96, B, 4, 0, E + 8, None) == ALIGN
+    assert ld(C, D, 10, 2, 128, B, 0, 0, E, None) == SHAPE
+    assert ld(C, D, 10, 2, 128, B, 4, 2, C + 1024, None) == ALIAS  # out over the cache
 
 
 @no_gpu_only
