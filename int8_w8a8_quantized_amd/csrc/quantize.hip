@@ -361,9 +361,12 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
 // Store: each (token, head) vector of head_dim elements is quantised as an
 // FP8 activation row (absmax / qmax, the same division and encoding) and
 // written to cache row slot[token] * heads + head.  P lanes (a power of two,
-// 8 elements each, P * 8 >= head_dim) hold one vector, 64 / P vectors per
-// wave; the absmax is combined over the vector's lanes by shuffles.  A slot
-// outside [0, slots) is not written.
+// 8 elements each, P * 8 >= head_dim) hold one vector; a workgroup takes
+// KV_U rounds of 256 / P vectors, all loads first so that KV_U are in
+// flight per lane.  The absmax is combined over the vector's lanes by
+// shuffles.  A slot outside [0, slots) is not written.
+constexpr int KV_U = 4;
+
 template <int P>
 __global__ __launch_bounds__(256) void kv_store_kernel(
     const uint16_t* __restrict__ kv, int64_t tokens, int heads, int hd, int64_t ld_token,
@@ -371,25 +374,36 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
     float* __restrict__ scale)
 {
     // (tokens * heads <= 2^30: 32-bit vector indices)
-    const int v = (int)blockIdx.x * (256 / P) + (int)threadIdx.x / P;
+    const int nv = (int)(tokens * heads);
     const int li = threadIdx.x % P;
-    const bool in = v < (int)(tokens * heads);
-    const int tok = in ? v / heads : 0;
-    const int h = in ? v - tok * heads : 0;
-    const bool act = in && li < (hd >> 3);
-    const uint4 x = act ? reinterpret_cast<const uint4*>(kv + (int64_t)tok * ld_token + (int64_t)h * hd)[li]
-                        : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t m = abs_max_chunk(0u, x);
-    m = max(m & 0xFFFFu, m >> 16);
+    const bool lane_on = li < (hd >> 3);
+    uint4 x[KV_U];
+    int tok[KV_U], h[KV_U];
+    bool in[KV_U];
 #pragma unroll
-    for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    const float s = __uint_as_float(m << 16) / qmax;  // correctly rounded (IEEE division)
-    const int64_t sl = in ? (int64_t)slot[tok] : -1;
-    if (act && sl >= 0 && sl < slots) {
-        const int64_t row = sl * heads + h;
-        const Quotient d(s);
-        reinterpret_cast<uint2*>(cache + row * hd)[li] = encode_chunk<kE4M3FN>(x, d, qmax);
-        if (li == 0) scale[row] = s;
+    for (int u = 0; u < KV_U; ++u) {
+        const int v = ((int)blockIdx.x * KV_U + u) * (256 / P) + (int)threadIdx.x / P;
+        in[u] = v < nv;
+        tok[u] = in[u] ? v / heads : 0;
+        h[u] = in[u] ? v - tok[u] * heads : 0;
+        x[u] = (in[u] && lane_on)
+                   ? reinterpret_cast<const uint4*>(kv + (int64_t)tok[u] * ld_token + (int64_t)h[u] * hd)[li]
+                   : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < KV_U; ++u) {
+        uint32_t m = abs_max_chunk(0u, x[u]);
+        m = max(m & 0xFFFFu, m >> 16);
+#pragma unroll
+        for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        const float s = __uint_as_float(m << 16) / qmax;  // correctly rounded (IEEE division)
+        const int64_t sl = in[u] ? (int64_t)slot[tok[u]] : -1;
+        if (lane_on && sl >= 0 && sl < slots) {
+            const int64_t row = sl * heads + h[u];
+            const Quotient d(s);
+            reinterpret_cast<uint2*>(cache + row * hd)[li] = encode_chunk<kE4M3FN>(x[u], d, qmax);
+            if (li == 0) scale[row] = s;
+        }
     }
 }
 
@@ -397,7 +411,8 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
 // index[i] * heads + head -- the E4M3FN decode is exact, the product is one
 // binary32 multiplication (RNE), then one conversion to the output type
 // (RNE).  An index outside [0, slots) gives a zero vector.  P threads (a
-// power of two, 8 elements each) per vector.
+// power of two, 8 elements each) per vector, KV_U rounds per workgroup with
+// all loads first.
 typedef float v2f_q __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_q __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h_q __attribute__((ext_vector_type(2)));
@@ -408,41 +423,54 @@ __global__ __launch_bounds__(256) void kv_load_kernel(
     int hd, const int32_t* __restrict__ index, int64_t n, void* __restrict__ out)
 {
     // (n * heads <= 2^30: 32-bit vector indices)
-    const int vec = (int)blockIdx.x * (256 / P) + (int)threadIdx.x / P;
+    const int nv = (int)(n * heads);
     const int ci = threadIdx.x % P;
-    if (vec >= (int)(n * heads) || ci >= (hd >> 3)) return;
-    const int i = vec / heads;
-    const int h = vec - i * heads;
-    const int64_t sl = index[i];
-    v2f_q f[4];
-    if (sl >= 0 && sl < slots) {
-        const int64_t row = sl * heads + h;
-        const uint2 q = reinterpret_cast<const uint2*>(cache + row * hd)[ci];
-        const float s = scale[row];
-        f[0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false) * s;
-        f[1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true) * s;
-        f[2] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false) * s;
-        f[3] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true) * s;
-    } else {
+    if (ci >= (hd >> 3)) return;
+    int vec[KV_U];
+    uint2 q[KV_U];
+    float s[KV_U];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) f[k] = v2f_q{0.0f, 0.0f};
-    }
-    const int64_t e0 = (int64_t)vec * hd + ci * 8;
-    if constexpr (OUT == 2) {
-        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
-        o[0] = make_float4(f[0].x, f[0].y, f[1].x, f[1].y);
-        o[1] = make_float4(f[2].x, f[2].y, f[3].x, f[3].y);
-    } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if constexpr (OUT == 0)
-                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2bf_q));
-            else
-                w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2h_q));
+    for (int u = 0; u < KV_U; ++u) {
+        vec[u] = ((int)blockIdx.x * KV_U + u) * (256 / P) + (int)threadIdx.x / P;
+        q[u] = make_uint2(0u, 0u);
+        s[u] = 0.0f;
+        if (vec[u] < nv) {
+            const int i = vec[u] / heads;
+            const int h = vec[u] - i * heads;
+            const int64_t sl = index[i];
+            if (sl >= 0 && sl < slots) {
+                const int64_t row = sl * heads + h;
+                q[u] = reinterpret_cast<const uint2*>(cache + row * hd)[ci];
+                s[u] = scale[row];
+            }
         }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < KV_U; ++u) {
+        if (vec[u] >= nv) continue;
+        // (a zero vector: codes 0 times scale 0)
+        v2f_q f[4];
+        f[0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[u].x, false) * s[u];
+        f[1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[u].x, true) * s[u];
+        f[2] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[u].y, false) * s[u];
+        f[3] = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[u].y, true) * s[u];
+        const int64_t e0 = (int64_t)vec[u] * hd + ci * 8;
+        if constexpr (OUT == 2) {
+            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+            o[0] = make_float4(f[0].x, f[0].y, f[1].x, f[1].y);
+            o[1] = make_float4(f[2].x, f[2].y, f[3].x, f[3].y);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (OUT == 0)
+                    w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2bf_q));
+                else
+                    w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[k], v2h_q));
+            }
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) =
+                make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -596,7 +624,7 @@ hipError_t launch_kv_store(const uint16_t* kv, int64_t tokens, int heads, int hd
     const int lanes = (hd + 7) / 8;
     const int64_t nvec = tokens * heads;
 #define TFQ_KV_STORE(P)                                                                           \
-    hipLaunchKernelGGL((kv_store_kernel<P>), dim3((unsigned)((nvec + 256 / P - 1) / (256 / P))),   \
+    hipLaunchKernelGGL((kv_store_kernel<P>), dim3((unsigned)((nvec + KV_U * 256 / P - 1) / (KV_U * 256 / P))), \
                        dim3(256), 0, stream, kv, tokens, heads, hd, ld_token, slot, slots, qmax,    \
                        cache, scale)
     if (lanes <= 4)
@@ -620,7 +648,7 @@ hipError_t launch_kv_load(const uint8_t* cache, const float* scale, int64_t slot
     const int lanes = (hd + 7) / 8;
     const int64_t nvec = n * heads;
 #define TFQ_KV_LOAD(O, P)                                                                         \
-    hipLaunchKernelGGL((kv_load_kernel<O, P>), dim3((unsigned)((nvec + 256 / P - 1) / (256 / P))), \
+    hipLaunchKernelGGL((kv_load_kernel<O, P>), dim3((unsigned)((nvec + KV_U * 256 / P - 1) / (KV_U * 256 / P))), \
                        dim3(256), 0, stream, cache, scale, slots, heads, hd, index, n, out)
 #define TFQ_KV_LOAD_P(O)       \
     if (lanes <= 4)            \
