@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 4
+#define TFQ_ABI_VERSION 5
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -319,6 +319,37 @@ tfq_status tfq_kv_cache_store(const void* kv_bf16, int64_t tokens, int64_t heads
 tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int64_t slots,
                              int64_t heads, int64_t head_dim, const int32_t* slot_index, int64_t n,
                              int32_t out_dtype, void* out, void* stream);
+
+/*
+ * Per-exact-shape autotuning of the GEMM launch configuration.  LightX2V
+ * "模型量化技术", "MiniMax-H3 FP8 FP16 累加" (tile and swizzle tuned per exact
+ * GEMM shape on first sight, winner kept in an in-process C++ cache, warm-up
+ * absorbing the first call, nothing written to disk).
+ *
+ * mode 0 (default): every GEMM entry point uses a fixed heuristic
+ * configuration.  mode 1: the first call of each (device, kind, m, n, k,
+ * epilogue, groups) shape times every candidate configuration (tile order
+ * band height; tile shape for small grids) on the caller's buffers and
+ * stream, caches the fastest and uses it from then on.  That first call
+ * waits for the stream; a stream being captured into a graph is never tuned
+ * (the cached or the heuristic configuration is used).  Every configuration
+ * produces the same result bits.  Other values: TFQ_ERR_UNSUPPORTED.
+ */
+tfq_status tfq_set_autotune(int32_t mode);
+
+/*
+ * The cached configuration of a shape, if any: returns 1 and writes kernel
+ * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU) and band (tile rows per
+ * band of the tile order), else 0.  kind: 0 FP8 per channel
+ * (tfq_scaled_mm_fp8, scale_block 0, and the fused FP8 Linear), 1 INT8,
+ * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`).  Looks up the
+ * current device's entries.
+ */
+int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
+                            int32_t groups, int32_t* kernel, int32_t* band);
+
+/* Forget every cached configuration. */
+void tfq_autotune_clear(void);
 
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream);
 

@@ -24,7 +24,8 @@ __all__ = [
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
     "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
     "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
-    "tfq_kv_cache_load", "KV_DTYPE",
+    "tfq_kv_cache_load", "KV_DTYPE", "tfq_set_autotune", "tfq_autotune_lookup",
+    "tfq_autotune_clear",
     "tfq_abi_version", "QuantLinear",
 ]
 
@@ -238,6 +239,30 @@ def tfq_kv_cache_load(cache: torch.Tensor, cache_scale: torch.Tensor, slot_index
                                   _ptr(slot_index), n, KV_DTYPE[out.dtype], _ptr(out),
                                   _stream(stream)), "tfq_kv_cache_load")
     return out
+
+
+def tfq_set_autotune(mode: int) -> None:
+    """0: fixed heuristic GEMM configurations (default); 1: tune each GEMM
+    shape on its first call and cache the winner in this process."""
+    check(lib().tfq_set_autotune(int(mode)), "tfq_set_autotune")
+
+
+AUTOTUNE_KIND = {"fp8": 0, "int8": 1, "fp8_block": 2, "mxfp8": 3, "grouped_fp8": 4}
+
+
+def tfq_autotune_lookup(kind, m: int, n: int, k: int, epi=None, groups: int = 0):
+    """(kernel, band) cached for a GEMM shape on the current device, or None."""
+    import ctypes
+
+    kern, band = ctypes.c_int32(0), ctypes.c_int32(0)
+    kd = AUTOTUNE_KIND[kind] if isinstance(kind, str) else int(kind)
+    found = lib().tfq_autotune_lookup(kd, m, n, k, _epi(epi), int(groups), ctypes.byref(kern),
+                                      ctypes.byref(band))
+    return (kern.value, band.value) if found else None
+
+
+def tfq_autotune_clear() -> None:
+    lib().tfq_autotune_clear()
 
 
 def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):

@@ -45,6 +45,9 @@ SIGNATURES = [
     ("tfq_scaled_mm_mxfp8", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _P]),
     ("tfq_kv_cache_store", _I32, [_P, _I64, _I64, _I64, _I64, _P, _I64, _F, _P, _P, _P]),
     ("tfq_kv_cache_load", _I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _I32, _P, _P]),
+    ("tfq_set_autotune", _I32, [_I32]),
+    ("tfq_autotune_lookup", _I32, [_I32, _I64, _I64, _I64, _I32, _I32, _P, _P]),
+    ("tfq_autotune_clear", None, []),
     ("tfq_e4m3fn_encode_f32", _I32, [_P, _P, _I64, _P]),
     ("tfq_status_string", ctypes.c_char_p, [_I32]),
     ("tfq_last_hip_error", ctypes.c_int, []),

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtfq.so")
 
-SOURCES = ["abi.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "tune.cpp", "quantize.hip", "gemm.hip"]
 HEADERS = ["tfq_internal.h"]
 
 ARCH = "gfx950"

@@ -440,6 +440,43 @@ tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int
                                           slot_index, n, out_dtype, out, (hipStream_t)stream));
 }
 
+tfq_status tfq_set_autotune(int32_t mode)
+{
+    if (mode != 0 && mode != 1) return TFQ_ERR_UNSUPPORTED;
+    tfq::set_autotune(mode);
+    return TFQ_OK;
+}
+
+int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
+                            int32_t groups, int32_t* kernel, int32_t* band)
+{
+    tfq::GemmArgs g{};
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.epi = epi;
+    switch (kind) {
+    case 0: g.qtype = tfq::kE4M3FN; break;
+    case 1: g.qtype = tfq::kInt8; break;
+    case 2: g.qtype = tfq::kE4M3FN; g.scale_block = 128; break;
+    case 3: g.qtype = tfq::kMxE4M3; break;
+    case 4: g.qtype = tfq::kE4M3FN; g.groups = groups; break;
+    default: return 0;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    tfq::GemmConfig c;
+    if (!tfq::autotune_lookup(dev, g, &c)) return 0;
+    if (kernel) *kernel = c.kernel;
+    if (band) *band = c.band;
+    return 1;
+}
+
+void tfq_autotune_clear(void) { tfq::autotune_clear(); }
+
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream)
 {
     if (!x || !q) return TFQ_ERR_NULL_POINTER;

@@ -1069,7 +1069,35 @@ int band_rows(int64_t m, int64_t n, int64_t k)
 
 }  // namespace
 
-hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
+// Heuristic launch configuration: the 256x128 two-per-CU kernel for grids of
+// fewer 256x256 tiles than CUs (the big-tile kernel would leave CUs idle),
+// else the 256x256 kernel; band height by K (band_rows).
+GemmConfig default_config(const GemmArgs& g)
+{
+    const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
+    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && g.qtype != kMxE4M3;
+    return GemmConfig{dual_ok && tiles < 256 ? 1 : 0, band_rows(g.m, g.n, g.k)};
+}
+
+int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
+{
+    static const int bands[4] = {1, 2, 4, 8};
+    int n = 0;
+    const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
+    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && g.qtype != kMxE4M3;
+    for (int kernel = 0; kernel < 2; ++kernel) {
+        // the two-per-CU kernel only where the grid is small enough to gain
+        if (kernel == 1 && !(dual_ok && tiles < 512)) continue;
+        for (int b : bands)
+            if (n < max_out) out[n++] = GemmConfig{kernel, b};
+    }
+    return n;
+}
+
+// Every configuration sums every output in the same order (same MFMAs, same
+// K stages, only the tile order or tile shape differs), so the choice never
+// changes a result bit.
+hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t stream)
 {
     Params p;
     p.a = g.a;
@@ -1086,7 +1114,7 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     p.k = (int)g.k;
     p.tiles_m = (int)((g.m + BM - 1) / BM);
     p.tiles_n = (int)((g.n + BN - 1) / BN);
-    p.group_m = band_rows(g.m, g.n, g.k);
+    p.group_m = c.band;
     p.goff = g.group_offsets;
     p.groups = g.groups;
     if (g.groups > 0) {
@@ -1109,11 +1137,7 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
     if (g.qtype == kMxE4M3)
         return g.epi == 1 ? launch_pipe<kMxE4M3, 1, true, false>(p, stream)
                           : launch_pipe<kMxE4M3, 0, true, false>(p, stream);
-    // Kernel choice by shape: with fewer 256x256 tiles than the 256 CUs the
-    // big-tile kernel leaves CUs idle, so the 256x128 two-per-CU kernel takes
-    // those problems.  Both sum every output in the same order (same MFMAs,
-    // same 64-deep K stages), so the choice never changes a result bit.
-    const bool dual = p.tiles_m * p.tiles_n < 256;
+    const bool dual = c.kernel == 1;
     const bool y = g.y != nullptr, a = g.acc != nullptr;
     if (g.qtype == kE4M3FN) {
         if (dual)

@@ -65,6 +65,26 @@ struct GemmArgs {
     int groups;            // 0 = not grouped
 };
 
+// A GEMM launch configuration: kernel 0 = 256x256 tiles, 1 = 256x128 tiles
+// two per CU (per-channel FP8 / INT8 only); band = tile rows per band of the
+// tile order.  Every configuration gives the same result bits.
+struct GemmConfig {
+    int kernel;
+    int band;
+};
+
+GemmConfig default_config(const GemmArgs& g);
+// the configurations the autotuner times for g (at most max_out)
+int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out);
+hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t stream);
+// the library's GEMM launch: the autotuned configuration if autotuning is on
+// (tune.cpp), else default_config
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);
+
+// autotune mode (0 off, 1 on), cache lookup and reset (tune.cpp)
+void set_autotune(int mode);
+int autotune_mode();
+bool autotune_lookup(int dev, const GemmArgs& g, GemmConfig* out);
+void autotune_clear();
 
 }  // namespace tfq

@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 4
+    assert L.tfq_abi_version() == 5
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -186,6 +186,14 @@ def test_kv_cache_validation(L):
     assert ld(C, D, 10, 2, 96, B, 4, 0, E + 8, None) == ALIGN
     assert ld(C, D, 10, 2, 128, B, 0, 0, E, None) == SHAPE
     assert ld(C, D, 10, 2, 128, B, 4, 2, C + 1024, None) == ALIAS  # out over the cache
+
+
+def test_autotune_switch_and_empty_cache(L):
+    assert L.tfq_set_autotune(2) == UNSUP and L.tfq_set_autotune(-1) == UNSUP
+    assert L.tfq_set_autotune(1) == OK and L.tfq_set_autotune(0) == OK
+    L.tfq_autotune_clear()
+    assert L.tfq_autotune_lookup(0, 4096, 4096, 4096, 0, 0, None, None) == 0
+    assert L.tfq_autotune_lookup(9, 4096, 4096, 4096, 0, 0, None, None) == 0  # unknown kind
 
 
 @no_gpu_only
