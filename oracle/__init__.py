@@ -84,6 +84,16 @@ def lib():
         L.tfq_oracle_quantize_mx.argtypes = [P, i64, i64, i64, P, P]
         L.tfq_oracle_linear_mx_ref.restype = None
         L.tfq_oracle_linear_mx_ref.argtypes = [P, P, P, P, i64, i64, i64, P, ctypes.c_int, P, i64, P]
+        L.tfq_oracle_e2m1_value.restype = ctypes.c_double
+        L.tfq_oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.tfq_oracle_e2m1_encode.restype = ctypes.c_uint8
+        L.tfq_oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.tfq_oracle_mx4_scale_code.restype = ctypes.c_uint8
+        L.tfq_oracle_mx4_scale_code.argtypes = [ctypes.c_float]
+        L.tfq_oracle_quantize_mx4.restype = None
+        L.tfq_oracle_quantize_mx4.argtypes = [P, i64, i64, i64, P, P]
+        L.tfq_oracle_linear_mx4_ref.restype = None
+        L.tfq_oracle_linear_mx4_ref.argtypes = [P, P, P, P, i64, i64, i64, P, ctypes.c_int, P, i64, P]
         L.tfq_oracle_int8_linear.restype = None
         L.tfq_oracle_int8_linear.argtypes = [P, P, P, P, i64, i64, i64, P, P, i64, P, P]
         L.tfq_oracle_error_measures.restype = None
@@ -373,6 +383,53 @@ def kv_load(cache: np.ndarray, scale: np.ndarray, index, out_dtype: str = "bf16"
         with np.errstate(over="ignore"):  # beyond FP16's range: infinity
             return prod.astype(np.float16).view(np.uint16)
     raise ValueError(out_dtype)
+
+
+def e2m1_value(code: int) -> float:
+    """E2M1 (FP4) value of the low 4 bits of code."""
+    return lib().tfq_oracle_e2m1_value(code)
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().tfq_oracle_e2m1_encode(v))
+
+
+def mx4_scale_code(amax: float) -> int:
+    """E8M0 byte of an MXFP4 block with largest magnitude amax (OCP MX v1.0 rule)."""
+    return int(lib().tfq_oracle_mx4_scale_code(float(amax)))
+
+
+def quantize_mx4(x_bf16: np.ndarray):
+    """MXFP4 quantisation of BF16 rows: (codes uint8 [R, C/2], two per byte,
+    lower index in the low nibble; E8M0 scales uint8 [R, C/32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    R, C = x.shape
+    assert C % 32 == 0
+    q = np.empty((R, C // 2), dtype=np.uint8)
+    s = np.empty((R, C // 32), dtype=np.uint8)
+    lib().tfq_oracle_quantize_mx4(_ptr(x), R, C, C, _ptr(q), _ptr(s))
+    return q, s
+
+
+def linear_mx4_ref(a_q, a_scale, b_q, b_scale, bias=None, gelu: bool = False,
+                   rows=None) -> np.ndarray:
+    """MXFP4 Linear reference y [R, N] in binary64 (see tfq_oracle_linear_mx4_ref)."""
+    a = np.ascontiguousarray(a_q, dtype=np.uint8)
+    b = np.ascontiguousarray(b_q, dtype=np.uint8)
+    M, K2 = a.shape
+    N = b.shape[0]
+    K = 2 * K2
+    assert b.shape[1] == K2 and K % 32 == 0
+    sa = np.ascontiguousarray(a_scale, dtype=np.uint8)
+    sb = np.ascontiguousarray(b_scale, dtype=np.uint8)
+    assert sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    out = np.empty((R, N), dtype=np.float64)
+    lib().tfq_oracle_linear_mx4_ref(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(bi),
+                                    1 if gelu else 0, _ptr(r), nr, _ptr(out))
+    return out
 
 
 def int8_linear(a_q, a_scale, b_q, b_scale, bias=None, rows=None, want_acc=True,

@@ -437,6 +437,114 @@ void tfq_oracle_linear_mx_ref(const uint8_t* a, const uint8_t* a_scale, const ui
     }
 }
 
+/* ---- MXFP4 ----
+ * OCP Microscaling (MX) v1.0 with E2M1 elements: 1 sign bit, 2 exponent
+ * bits (bias 1) and 1 mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ * one E8M0 scale per 32 elements (TeleFuser "Quantization", converter
+ * section: MXFP4/6/8 use 32-value blocks and E8M0 scales).  Shared exponent
+ * floor(log2(amax)) - 2 (2 = the exponent of E2M1's largest normal, 6 =
+ * 1.5 * 2^2), clamped to [-127, 127]; elements v / 2^shared clamped to +-6
+ * and rounded to the nearest E2M1 value, ties to the even code.  Two codes
+ * per byte, the element with the lower index in the low nibble. */
+static const double kE2M1Mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double tfq_oracle_e2m1_value(uint8_t code)
+{
+    const double v = kE2M1Mag[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest E2M1 code of t (saturating at 6; ties to the even code; the sign
+ * is kept, also for results of zero). */
+uint8_t tfq_oracle_e2m1_encode(float t)
+{
+    const int neg = signbit(t) != 0;
+    double a = fabs((double)t);
+    if (a > 6.0) a = 6.0;
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        const double d = fabs(a - kE2M1Mag[c]);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (uint8_t)(best | (neg ? 8 : 0));
+}
+
+uint8_t tfq_oracle_mx4_scale_code(float amax)
+{
+    int e;
+    if (!(amax > 0.0f)) return 0;            /* zero block: 2^-127 */
+    (void)frexpf(amax, &e);                   /* amax = f * 2^e, f in [0.5, 1) */
+    int shared = (e - 1) - 2;                 /* floor(log2 amax) - emax_elem */
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
+/* Quantise rows of BF16 x [rows, cols] (cols % 32 == 0, leading dim ld) to
+ * MXFP4: packed codes [rows, cols / 2] and E8M0 scales [rows, cols / 32]. */
+void tfq_oracle_quantize_mx4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                             uint8_t* q, uint8_t* scale)
+{
+    const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t i = 0; i < cols / 2; ++i) q[r * (cols / 2) + i] = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + r * ld + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(tfq_oracle_bf16_to_f32(xb[i]));
+                if (a > amax) amax = a;
+            }
+            const uint8_t code = tfq_oracle_mx4_scale_code(amax);
+            scale[r * nb + b] = code;
+            const double X = ldexp(1.0, (int)code - 127);
+            for (int i = 0; i < 32; ++i) {
+                const float t = (float)((double)tfq_oracle_bf16_to_f32(xb[i]) / X);
+                const int64_t e = b * 32 + i;
+                q[r * (cols / 2) + e / 2] |= (uint8_t)(tfq_oracle_e2m1_encode(t) << (4 * (e & 1)));
+            }
+        }
+    }
+}
+
+/* MXFP4 Linear reference in binary64 for selected rows (codes packed two
+ * per byte; as tfq_oracle_linear_mx_ref otherwise). */
+void tfq_oracle_linear_mx4_ref(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                               const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
+                               const uint16_t* bias, int epi, const int64_t* rows, int64_t nrows,
+                               double* y)
+{
+    const int64_t R = rows ? nrows : M;
+    const int64_t nb = K / 32, kb2 = K / 2;
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < R; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+        for (int64_t k = 0; k < K; ++k)
+            arow[k] = tfq_oracle_e2m1_value((uint8_t)(a[m * kb2 + k / 2] >> (4 * (k & 1))));
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            for (int64_t kb = 0; kb < nb; ++kb) {
+                double acc = 0.0;
+                for (int64_t k = kb * 32; k < kb * 32 + 32; ++k)
+                    acc += arow[k] *
+                           tfq_oracle_e2m1_value((uint8_t)(b[n * kb2 + k / 2] >> (4 * (k & 1))));
+                v += ldexp(acc, (int)a_scale[m * nb + kb] - 127 + (int)b_scale[n * nb + kb] - 127);
+            }
+            if (bias) v += (double)tfq_oracle_bf16_to_f32(bias[n]);
+            if (epi == 1) v = tfq_oracle_gelu_tanh(v);
+            y[i * N + n] = v;
+        }
+        free(arow);
+    }
+}
+
 /* INT8 W8A8: exact INT32 accumulators (held in int64 here; the caller keeps
  * K small enough that they fit INT32) and the fixed-order BF16 output.
  * acc and y_bf16 may each be NULL. */
