@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 5
+#define TFQ_ABI_VERSION 6
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -285,6 +285,43 @@ tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, cons
                                const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
 
 /*
+ * MXFP4 quantisation: E2M1 codes (1 sign, 2 exponent bits with bias 1, 1
+ * mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0 scale
+ * byte per 32 consecutive elements of a row.  TeleFuser "Quantization",
+ * converter section (MXFP4 uses 32-value blocks with E8M0 scales); OCP MX
+ * v1.0 block rule: shared exponent floor(log2(amax)) - 2 (6 = 1.5 * 2^2),
+ * clamped to [-127, 127], scale byte = shared + 127; codes = nearest E2M1
+ * value of clamp(x * 2^-shared, +-6), ties to the even code, sign kept.
+ *
+ *   x_bf16    [rows, cols] BF16 as tfq_quantize_mx.
+ *   q_out     [rows, cols/2] bytes, two codes each, the element with the
+ *             lower index in the low nibble; 16-byte aligned.
+ *   scale_out [cols/128, rows] scale words in the layout of
+ *             tfq_quantize_mx.
+ *   rows >= 1; cols >= 128, cols % 128 == 0; rows * cols / 32 <= 2^30.
+ */
+tfq_status tfq_quantize_mxfp4(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              void* q_out, uint32_t* scale_out, void* stream);
+
+/*
+ * MXFP4 GEMM: y[m,n] = sum over 32-blocks kb of 2^(ea[m,kb] - 127)
+ * 2^(eb[n,kb] - 127) sum_{k in kb} a[m,k] b[n,k] over E2M1 values,
+ * accumulated in FP32 by the matrix cores, rounded once to BF16, bias and
+ * epilogue as for tfq_scaled_mm_fp8.  TeleFuser "Quantization", converter
+ * section (MXFP4 block format).
+ *
+ *   a_q [m, k/2], b_q [n, k/2] packed E2M1 codes (as tfq_quantize_mxfp4
+ *   writes them), 16-byte aligned; a_scale [k/128, m], b_scale [k/128, n]
+ *   scale words as for tfq_scaled_mm_mxfp8.
+ *   bias_bf16 [n] or NULL; epi tfq_epilogue; y_bf16 [m, n] BF16.
+ *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 8388608, k % 128 == 0;
+ *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
+ */
+tfq_status tfq_scaled_mm_mxfp4(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
+                               const uint32_t* b_scale, int64_t m, int64_t n, int64_t k,
+                               const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
+
+/*
  * FP8 KV cache.  TeleFuser "Quantization", "Other quantized data paths"
  * (LiveAct FP8 KV cache: K/V stored as E4M3FN with one FP32 scale per
  * last-dimension vector, dequantised to the requested attention dtype on
@@ -342,7 +379,7 @@ tfq_status tfq_set_autotune(int32_t mode);
  * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU) and band (tile rows per
  * band of the tile order), else 0.  kind: 0 FP8 per channel
  * (tfq_scaled_mm_fp8, scale_block 0, and the fused FP8 Linear), 1 INT8,
- * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`).  Looks up the
+ * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4.  Looks up the
  * current device's entries.
  */
 int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,

@@ -25,7 +25,7 @@ __all__ = [
     "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
     "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
     "tfq_kv_cache_load", "KV_DTYPE", "tfq_set_autotune", "tfq_autotune_lookup",
-    "tfq_autotune_clear",
+    "tfq_autotune_clear", "tfq_quantize_mxfp4", "tfq_scaled_mm_mxfp4",
     "tfq_abi_version", "QuantLinear",
 ]
 
@@ -247,7 +247,7 @@ def tfq_set_autotune(mode: int) -> None:
     check(lib().tfq_set_autotune(int(mode)), "tfq_set_autotune")
 
 
-AUTOTUNE_KIND = {"fp8": 0, "int8": 1, "fp8_block": 2, "mxfp8": 3, "grouped_fp8": 4}
+AUTOTUNE_KIND = {"fp8": 0, "int8": 1, "fp8_block": 2, "mxfp8": 3, "grouped_fp8": 4, "mxfp4": 5}
 
 
 def tfq_autotune_lookup(kind, m: int, n: int, k: int, epi=None, groups: int = 0):
@@ -263,6 +263,32 @@ def tfq_autotune_lookup(kind, m: int, n: int, k: int, epi=None, groups: int = 0)
 
 def tfq_autotune_clear() -> None:
     lib().tfq_autotune_clear()
+
+
+def tfq_quantize_mxfp4(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
+    """MXFP4 quantisation of BF16 rows x [rows, cols]: returns (packed E2M1
+    codes uint8 [rows, cols/2], lower index in the low nibble; E8M0 scales
+    uint8 [cols/128, rows, 4] as tfq_quantize_mx)."""
+    rows, cols = x.shape
+    if q_out is None:
+        q_out = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=x.device)
+    check(lib().tfq_quantize_mxfp4(_ptr(x), rows, cols, x.stride(0), _ptr(q_out), _ptr(scale_out),
+                                   _stream(stream)), "tfq_quantize_mxfp4")
+    return q_out, scale_out
+
+
+def tfq_scaled_mm_mxfp4(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None, stream=None):
+    """y [m, n] BF16 from MXFP4 operands a_q [m, k/2], b_q [n, k/2] (packed)."""
+    m, k2 = a_q.shape
+    n = b_q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    check(lib().tfq_scaled_mm_mxfp4(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n,
+                                    2 * k2, _ptr(bias), _epi(epi), _ptr(y), _stream(stream)),
+          "tfq_scaled_mm_mxfp4")
+    return y
 
 
 def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):

@@ -204,12 +204,19 @@ template <>
 struct PipeAcc<kMxE4M3> {
     typedef v16f type;
 };
+template <>
+struct PipeAcc<kMxE2M1> {
+    typedef v16f type;
+};
 
 template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_pipe_kernel(const Params p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[PSMEM];
+    // MXFP4 rows hold two codes per byte: K counts bytes below, and a stage
+    // (128 bytes) holds 256 elements = two 128-element scale groups
+    constexpr bool FP4 = QT == kMxE2M1;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[FP4 ? PSMEM + 2 * 2048 : PSMEM];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -280,7 +287,7 @@ void gemm_pipe_kernel(const Params p)
         m0 = tm * BM;
     }
     const int n0 = tn * BN;
-    const int K = p.k;
+    const int K = FP4 ? p.k / 2 : p.k;
     const int rows_a = min(BM, m_end - m0), rows_b = min(BN, p.n - n0);
     const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
     const v4i rb = buffer_rsrc(b_grp + (int64_t)n0 * K, rows_b * K);
@@ -362,7 +369,7 @@ void gemm_pipe_kernel(const Params p)
     // word holds the group's blocks in the byte order 0, 2, 1, 3, so lane
     // half h reads the 16 bits at byte 2 h -- blocks h and 2 + h -- and the
     // MFMA's byte select is ks for every lane (operand order as the data).
-    constexpr bool MX = QT == kMxE4M3;
+    constexpr bool MX = QT == kMxE4M3 || FP4;
     int scA[2][4], scB[2][4];
     auto mfma_one = [&](int mi, int ni, const Frags& f, int set = 0, int ks = 0) {
         if constexpr (QT == kE4M3FN) {
@@ -390,15 +397,23 @@ void gemm_pipe_kernel(const Params p)
     // in one piece (wave w loads rows 64 w + lane of A and of B).  Rows past
     // the end of A or B read the next group's words (finite scales of zero
     // data, in outputs that are never stored) or zeros past the tensor.
-    const int KG = K / PK;
+    // (MXFP4: a stage takes the words of groups 2 kt and 2 kt + 1, 4 KB per
+    // ring slot: A and B of the first group, then of the second)
+    const int KG = p.k / 128;  // 128-element scale groups
     const v4i rea = MX ? buffer_rsrc(p.ea + m0, (KG * p.m - m0) * 4) : v4i{};
     const v4i reb = MX ? buffer_rsrc(p.eb + n0, (KG * p.n - n0) * 4) : v4i{};
     auto dma_mx = [&](int kt) {
         const int r = 64 * wave + lane;
-        const bool pad = kt >= KG;
-        const uint32_t dst = lds_base + PMXS + (kt & (PMXRING - 1)) * 2048 + wave_u * 256;
-        lds_dma4(rea, pad ? (int)0x80000000u : (kt * p.m + r) * 4, dst);
-        lds_dma4(reb, pad ? (int)0x80000000u : (kt * p.n + r) * 4, dst + 1024);
+        constexpr int GPS = FP4 ? 2 : 1;  // scale groups per stage
+#pragma unroll
+        for (int gi = 0; gi < GPS; ++gi) {
+            const int grp = kt * GPS + gi;
+            const bool pad = grp >= KG;
+            const uint32_t dst =
+                lds_base + PMXS + (kt & (PMXRING - 1)) * (2048 * GPS) + gi * 2048 + wave_u * 256;
+            lds_dma4(rea, pad ? (int)0x80000000u : (grp * p.m + r) * 4, dst);
+            lds_dma4(reb, pad ? (int)0x80000000u : (grp * p.n + r) * 4, dst + 1024);
+        }
     };
     // (straight from LDS into the MFMA's scale operand: no VALU work, so the
     // reads need not complete before the MFMAs that do not use them)
@@ -410,6 +425,21 @@ void gemm_pipe_kernel(const Params p)
             scA[set][i] = sm[2 * (wm * 128 + i * 32 + fr) + h];
             scB[set][i] = sm[2 * (256 + wn * 128 + i * 32 + fr) + h];
         }
+    };
+    // MXFP4: the scale halves of both groups of a stage (group g = ks / 2 for
+    // K step ks; lane half h holds blocks h and 2 + h of the group, the
+    // MFMA's byte select is ks & 1)
+    int s4A[2][2][4], s4B[2][2][4];
+    auto read_mx4 = [&](int kt, int set) {
+        const uint16_t* sm =
+            reinterpret_cast<const uint16_t*>(smem + PMXS + (kt & (PMXRING - 1)) * 4096);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s4A[set][g][i] = sm[1024 * g + 2 * (wm * 128 + i * 32 + fr) + h];
+                s4B[set][g][i] = sm[1024 * g + 2 * (256 + wn * 128 + i * 32 + fr) + h];
+            }
     };
 #define TFQ_FENCE() __builtin_amdgcn_sched_barrier(0)
 
@@ -447,47 +477,132 @@ void gemm_pipe_kernel(const Params p)
         }
         if constexpr (MX) dma_mx(u);
     }
-    // stage 0 complete: the loads of stage 1 (16, plus 2 scale loads for
-    // MXFP8) may still be in flight
-    if constexpr (MX)
-        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    if constexpr (FP4) {
+        // MXFP4: a stage is four K steps of 64 elements.  In K step ks lane
+        // half h holds row (lane & 31)'s 16-byte chunk 2 ks + h -- one whole
+        // 32-element block, whose scale the lane passes (the MFMA reads
+        // registers 0-3 of each lane for E2M1).  Each K step reads the next
+        // one's fragments, one 16-byte read after every other MFMA; the
+        // stage's barrier comes before its last K step, which reads the next
+        // stage's first fragments and issues the loads of the stage after.
+        struct Frags4 {
+            v4i b[4], a[4];
+        };
+        int rd4[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        read_part(0, 0, f0, q, 0);
-        read_part(0, 0, f0, q, 1);
-    }
-    if constexpr (MX) read_mx(0, 0);
-
-    for (int kt = 0; kt < KT; kt += 2) {
+        for (int ks = 0; ks < 4; ++ks) rd4[ks] = fr * PK + (((2 * ks + h) ^ sw) << 4);
+        auto read4 = [&](int buf, int ks, Frags4& f, int q) {
+            const uint8_t* sp =
+                smem + buf * PSTAGE + (q < 4 ? b_rd + q * 32 * PK : a_rd + (q - 4) * 32 * PK);
+            const v4i v = *reinterpret_cast<const v4i*>(sp + rd4[ks]);
+            if (q < 4)
+                f.b[q] = v;
+            else
+                f.a[q - 4] = v;
+        };
+        auto mfma4 = [&](int mi, int ni, const Frags4& f, int set, int ks) {
+            const v8i bb = __builtin_shufflevector(f.b[ni], f.b[ni], 0, 1, 2, 3, -1, -1, -1, -1);
+            const v8i aa = __builtin_shufflevector(f.a[mi], f.a[mi], 0, 1, 2, 3, -1, -1, -1, -1);
+            const int g = ks >> 1;
+            if ((ks & 1) == 0)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bb, aa, acc[mi][ni], 4, 4, 0, s4B[set][g][ni], 0, s4A[set][g][mi]);
+            else
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bb, aa, acc[mi][ni], 4, 4, 1, s4B[set][g][ni], 1, s4A[set][g][mi]);
+        };
+        Frags4 g0, g1;
+        // stage 0 complete: stage 1's 16 data and 4 scale loads may still be
+        // in flight
+        asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            // K step 0 of stage kt+u from f0; K step 1's fragments into f1
+        for (int q = 0; q < 8; ++q) read4(0, 0, g0, q);
+        read_mx4(0, 0);
+        for (int kt = 0; kt < KT; kt += 2) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                mfma_one(i >> 2, i & 3, f0, u, 0);
-                TFQ_FENCE();
-                read_part(u, 1, f1, i >> 1, i & 1);
-                TFQ_FENCE();
-            }
-            // own loads of stage kt+u+1 (the only ones in flight) are done
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            // K step 1 from f1; stage kt+u+1's first fragments into f0 and
-            // the loads of stage kt+u+2
-            if constexpr (MX) read_mx(kt + u + 1, u ^ 1);
+            for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                mfma_one(i >> 2, i & 3, f1, u, 1);
-                TFQ_FENCE();
-                read_part(u ^ 1, 0, f0, i >> 1, i & 1);
-                if constexpr (MX)
-                    if (i == 0) dma_mx(kt + u + 2);
-                if (i < 8) {
-                    dma(kt + u + 2, 0, i);
-                    dma(kt + u + 2, 1, i);
+                for (int i = 0; i < 16; ++i) {
+                    mfma4(i >> 2, i & 3, g0, u, 0);
+                    TFQ_FENCE();
+                    if ((i & 1) == 0) read4(u, 1, g1, i >> 1);
+                    TFQ_FENCE();
                 }
-                TFQ_FENCE();
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma4(i >> 2, i & 3, g1, u, 1);
+                    TFQ_FENCE();
+                    if ((i & 1) == 0) read4(u, 2, g0, i >> 1);
+                    TFQ_FENCE();
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma4(i >> 2, i & 3, g0, u, 2);
+                    TFQ_FENCE();
+                    if ((i & 1) == 0) read4(u, 3, g1, i >> 1);
+                    TFQ_FENCE();
+                }
+                // own loads of stage kt+u+1 are done; every wave has read all
+                // of stage kt+u
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                read_mx4(kt + u + 1, u ^ 1);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma4(i >> 2, i & 3, g1, u, 3);
+                    TFQ_FENCE();
+                    if ((i & 1) == 0) read4(u ^ 1, 0, g0, i >> 1);
+                    if (i == 0) dma_mx(kt + u + 2);
+                    if (i < 8) {
+                        dma(kt + u + 2, 0, i);
+                        dma(kt + u + 2, 1, i);
+                    }
+                    TFQ_FENCE();
+                }
+            }
+        }
+    } else {
+        // stage 0 complete: the loads of stage 1 (16, plus 2 scale loads for
+        // MXFP8) may still be in flight
+        if constexpr (MX)
+            asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    #pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            read_part(0, 0, f0, q, 0);
+            read_part(0, 0, f0, q, 1);
+        }
+        if constexpr (MX) read_mx(0, 0);
+
+        for (int kt = 0; kt < KT; kt += 2) {
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                // K step 0 of stage kt+u from f0; K step 1's fragments into f1
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma_one(i >> 2, i & 3, f0, u, 0);
+                    TFQ_FENCE();
+                    read_part(u, 1, f1, i >> 1, i & 1);
+                    TFQ_FENCE();
+                }
+                // own loads of stage kt+u+1 (the only ones in flight) are done
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                // K step 1 from f1; stage kt+u+1's first fragments into f0 and
+                // the loads of stage kt+u+2
+                if constexpr (MX) read_mx(kt + u + 1, u ^ 1);
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mfma_one(i >> 2, i & 3, f1, u, 1);
+                    TFQ_FENCE();
+                    read_part(u ^ 1, 0, f0, i >> 1, i & 1);
+                    if constexpr (MX)
+                        if (i == 0) dma_mx(kt + u + 2);
+                    if (i < 8) {
+                        dma(kt + u + 2, 0, i);
+                        dma(kt + u + 2, 1, i);
+                    }
+                    TFQ_FENCE();
+                }
             }
         }
     }
@@ -1075,7 +1190,7 @@ int band_rows(int64_t m, int64_t n, int64_t k)
 GemmConfig default_config(const GemmArgs& g)
 {
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && g.qtype != kMxE4M3;
+    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && (g.qtype == kE4M3FN || g.qtype == kInt8);
     return GemmConfig{dual_ok && tiles < 256 ? 1 : 0, band_rows(g.m, g.n, g.k)};
 }
 
@@ -1084,7 +1199,7 @@ int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
     static const int bands[4] = {1, 2, 4, 8};
     int n = 0;
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && g.qtype != kMxE4M3;
+    const bool dual_ok = g.groups == 0 && g.scale_block == 0 && (g.qtype == kE4M3FN || g.qtype == kInt8);
     for (int kernel = 0; kernel < 2; ++kernel) {
         // the two-per-CU kernel only where the grid is small enough to gain
         if (kernel == 1 && !(dual_ok && tiles < 512)) continue;
@@ -1133,10 +1248,13 @@ hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t 
     }
     if (g.scale_block == 128)
         return g.epi == 1 ? launch_block<1>(p, stream) : launch_block<0>(p, stream);
-    // MXFP8 always takes the 256x256 kernel (its scale ring lives there)
+    // MXFP8 and MXFP4 always take the 256x256 kernel (its scale ring lives there)
     if (g.qtype == kMxE4M3)
         return g.epi == 1 ? launch_pipe<kMxE4M3, 1, true, false>(p, stream)
                           : launch_pipe<kMxE4M3, 0, true, false>(p, stream);
+    if (g.qtype == kMxE2M1)
+        return g.epi == 1 ? launch_pipe<kMxE2M1, 1, true, false>(p, stream)
+                          : launch_pipe<kMxE2M1, 0, true, false>(p, stream);
     const bool dual = c.kernel == 1;
     const bool y = g.y != nullptr, a = g.acc != nullptr;
     if (g.qtype == kE4M3FN) {

@@ -305,16 +305,44 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 // word (g, row) at g * rows + row -- the layout the MXFP8 GEMM loads whole
 // per K stage (each half of the word is what one half of an MFMA's lanes
 // needs).
+//
+// MXFP4 (F == 4): E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), shared
+// exponent floor(log2(amax)) - 2 (6 = 1.5 * 2^2), so the byte is
+// max(e - 2, 0); elements x * 2^-shared clamped to +-6 and rounded to the
+// nearest E2M1 value, ties to the even code.  Two codes per byte, the lower
+// index in the low nibble: a lane's 8 elements are one 32-bit store.
+__device__ __forceinline__ uint32_t e2m1_code(float t)
+{
+    // the thresholds are the midpoints of the grid; at a midpoint the even
+    // code wins (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+    // 3.5 -> 4, 5 -> 4), and everything above 5 saturates to 6
+    const float a = __builtin_fabsf(t);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(t) >> 28) & 8u);
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float inv)
+{
+    return e2m1_code(bf_lo(w.x) * inv) | (e2m1_code(bf_hi(w.x) * inv) << 4) |
+           (e2m1_code(bf_lo(w.y) * inv) << 8) | (e2m1_code(bf_hi(w.y) * inv) << 12) |
+           (e2m1_code(bf_lo(w.z) * inv) << 16) | (e2m1_code(bf_hi(w.z) * inv) << 20) |
+           (e2m1_code(bf_lo(w.w) * inv) << 24) | (e2m1_code(bf_hi(w.w) * inv) << 28);
+}
+
+template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1)
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
                                                           int64_t rows, int64_t cols, int64_t ld,
                                                           uint8_t* __restrict__ q,
                                                           uint32_t* __restrict__ scale)
 {
+    constexpr int kEmax = F == 8 ? 8 : 2;  // exponent of the element type's largest normal
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
-    uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    uint8_t* qrow = q + row * (F == 8 ? cols : cols / 2);
     const int nchunk = (int)(cols >> 3);  // a multiple of 16: whole groups only
     constexpr int U = 4;
     for (int base = 0; base < nchunk; base += 64 * U) {
@@ -332,7 +360,7 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
             // block max over the 4 lanes of the quad
             m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
             m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
-            const int code = max((int)((m >> 7) & 0xFFu) - 8, 0);
+            const int code = max((int)((m >> 7) & 0xFFu) - kEmax, 0);
             const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
             // the codes of the group's other 3 blocks (lanes +4, +8, +12 of the
             // 16-lane DPP row) into the group's first lane
@@ -342,12 +370,16 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
             if (idx < nchunk) {
                 const uint4 w = v[u];
-                uint2 o;
-                o.x = encode4<kE4M3FN>(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv,
-                                       bf_hi(w.y) * inv, 448.0f);
-                o.y = encode4<kE4M3FN>(bf_lo(w.z) * inv, bf_hi(w.z) * inv, bf_lo(w.w) * inv,
-                                       bf_hi(w.w) * inv, 448.0f);
-                qr[idx] = o;
+                if constexpr (F == 8) {
+                    uint2 o;
+                    o.x = encode4<kE4M3FN>(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv,
+                                           bf_hi(w.y) * inv, 448.0f);
+                    o.y = encode4<kE4M3FN>(bf_lo(w.z) * inv, bf_hi(w.z) * inv, bf_lo(w.w) * inv,
+                                           bf_hi(w.w) * inv, 448.0f);
+                    reinterpret_cast<uint2*>(qrow)[idx] = o;
+                } else {
+                    reinterpret_cast<uint32_t*>(qrow)[idx] = e2m1_pack8(w, inv);
+                }
                 if ((lane & 15) == 0) scale[(int64_t)(idx >> 4) * rows + row] = word;
             }
         }
@@ -596,11 +628,15 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 }
 
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                              uint8_t* q, uint32_t* scale, hipStream_t stream)
+                              uint8_t* q, uint32_t* scale, hipStream_t stream, int elem_bits)
 {
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows,
-                       cols, ld, q, scale);
+    if (elem_bits == 4)
+        hipLaunchKernelGGL((quantize_mx_kernel<4>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                           rows, cols, ld, q, scale);
+    else
+        hipLaunchKernelGGL((quantize_mx_kernel<8>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                           rows, cols, ld, q, scale);
     return hipGetLastError();
 }
 

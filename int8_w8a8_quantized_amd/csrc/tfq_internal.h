@@ -8,8 +8,9 @@
 
 namespace tfq {
 
-// kMxE4M3: E4M3FN codes with one E8M0 scale per 32 elements along K (MXFP8)
-enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2 };
+// kMxE4M3: E4M3FN codes with one E8M0 scale per 32 elements along K (MXFP8);
+// kMxE2M1: E2M1 codes, two per byte, with the same scales (MXFP4)
+enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2, kMxE2M1 = 3 };
 
 // Launchers enqueue kernels on `stream` and return the launch status.  They
 // assume the arguments already passed the host-side validation.
@@ -22,11 +23,11 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
                                 hipStream_t stream, const int32_t* gather = nullptr,
                                 int64_t src_rows = 0);
 
-// MXFP8 rows (cols % 128 == 0): codes [rows, cols], E8M0 scale words
-// [cols/128, rows] (bytes 0..3 of word (g, r) = blocks 4 g + 0, 2, 1, 3 of
-// row r)
+// MX rows (cols % 128 == 0): E8M0 scale words [cols/128, rows] (bytes 0..3
+// of word (g, r) = blocks 4 g + 0, 2, 1, 3 of row r); elem_bits 8: MXFP8 codes [rows, cols]; 4: MXFP4 codes [rows, cols/2], two
+// per byte (lower index in the low nibble)
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                              uint8_t* q, uint32_t* scale, hipStream_t stream);
+                              uint8_t* q, uint32_t* scale, hipStream_t stream, int elem_bits = 8);
 
 // FP8 KV cache: store kv [tokens, heads, hd] (token stride ld_token) into
 // cache rows slot[t] * heads + h; load rows index[i] dequantised to

@@ -62,3 +62,20 @@ def assert_fp8_tolerance(y_bits: np.ndarray, y_ref: np.ndarray, what: str = "") 
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(allow > 0, err / allow, 0.0)
     return float(ratio.max())
+
+
+# MX scale layout of the library: [cols/128, rows, 4], the four block scales
+# of a 128-element K group together in the byte order 0, 2, 1, 3
+MX_ORDER = [0, 2, 1, 3]
+
+
+def mx_grouped(s):
+    """Oracle scales [rows, cols/32] -> library layout [cols/128, rows, 4]."""
+    r, nb = s.shape
+    return np.ascontiguousarray(s.reshape(r, nb // 4, 4)[:, :, MX_ORDER].transpose(1, 0, 2))
+
+
+def mx_ungrouped(s):
+    """Library layout [cols/128, rows, 4] -> oracle scales [rows, cols/32]."""
+    g, r, _ = s.shape
+    return np.ascontiguousarray(s[:, :, MX_ORDER].transpose(1, 0, 2).reshape(r, 4 * g))

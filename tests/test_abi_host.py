@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 5
+    assert L.tfq_abi_version() == 6
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -135,6 +135,17 @@ def test_mx_validation(L):
     assert g(A + 4, B, C, D, 64, 64, 128, None, 0, E, None) == ALIGN
     assert g(A, B, C, D, 64, 64, 128, None, 0, E + 8, None) == ALIGN
     assert g(A, B, C, D, 64, 64, 128, None, 0, B + 16, None) == ALIAS  # y over a_scale
+    q4 = L.tfq_quantize_mxfp4
+    assert q4(A, 4, 128, 128, B, C, None) == DEV
+    assert q4(A, 4, 96, 96, B, C, None) == SHAPE           # cols % 128
+    assert q4(A, 4, 128, 128, B + 4, C, None) == ALIGN
+    assert q4(A, 4, 128, 128, B, B + 252, None) == ALIAS   # scales over the 256 code bytes
+    assert q4(A, 4, 128, 128, B, B + 256, None) == DEV
+    g4 = L.tfq_scaled_mm_mxfp4
+    assert g4(A, B, C, D, 64, 64, 128, None, 0, E, None) == DEV
+    assert g4(A, B, C, D, 64, 64, 192, None, 0, E, None) == SHAPE  # k % 128
+    assert g4(A, B, C, D, 64, 64, 128, None, 0, A + 64 * 64, None) == DEV   # after a_q's 64*64 bytes
+    assert g4(A, B, C, D, 64, 64, 128, None, 0, A + 64 * 48, None) == ALIAS
 
 
 @no_gpu_only

@@ -17,7 +17,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, needs_gpu, say
+from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, mx_grouped,
+                      mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -29,19 +30,7 @@ def tfq():
     return m
 
 
-ORDER = [0, 2, 1, 3]  # block (within a group of 4) held by each byte of a scale word
-
-
-def grouped(s):
-    """[rows, cols/32] -> [cols/128, rows, 4]."""
-    r, nb = s.shape
-    return np.ascontiguousarray(s.reshape(r, nb // 4, 4)[:, :, ORDER].transpose(1, 0, 2))
-
-
-def ungrouped(s):
-    """[cols/128, rows, 4] -> [rows, cols/32]."""
-    g, r, _ = s.shape
-    return np.ascontiguousarray(s[:, :, ORDER].transpose(1, 0, 2).reshape(r, 4 * g))
+grouped, ungrouped = mx_grouped, mx_ungrouped
 
 
 def _blocky(rng, rows, cols, sigma=1.0, spread=6):
