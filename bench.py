@@ -172,31 +172,37 @@ def extras(torch, tfq, synth, stream):
     return out
 
 
-def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y):
-    """The same FFN pair in MXFP8 (E8M0 scale per 32 elements, scales applied
-    by the scaled MFMA): each call timed on its own (median of 20)."""
-    log("extras: c4 FFN pair in MXFP8")
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (and FP6) MFMA
+
+
+def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, bits=8):
+    """The same FFN pair in MXFP8 (bits 8) or MXFP4 (bits 4): E8M0 scale per
+    32 elements, scales applied by the scaled MFMA; each call timed on its
+    own (median of 20)."""
+    log(f"extras: c4 FFN pair in MXFP{bits}")
     M, K = x.shape
     N, N2 = w_up.shape[0], w_dn.shape[0]
-    wq_up, ws_up = tfq.tfq_quantize_mx(w_up)
-    wq_dn, ws_dn = tfq.tfq_quantize_mx(w_dn)
-    qx, sx = tfq.tfq_quantize_mx(x)
-    qg, sg = tfq.tfq_quantize_mx(g)
+    quant = tfq.tfq_quantize_mx if bits == 8 else tfq.tfq_quantize_mxfp4
+    mm = tfq.tfq_scaled_mm_mxfp8 if bits == 8 else tfq.tfq_scaled_mm_mxfp4
+    peak = FP8_PEAK_TFLOPS if bits == 8 else FP4_PEAK_TFLOPS
+    wq_up, ws_up = quant(w_up)
+    wq_dn, ws_dn = quant(w_dn)
+    qx, sx = quant(x)
+    qg, sg = quant(g)
     out = {}
-    ms_qx, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_mx(x, qx, sx))
-    ms_up, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_mxfp8(qx, sx, wq_up, ws_up, None,
-                                                                          "gelu_tanh", g))
-    ms_qg, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_mx(g, qg, sg))
-    ms_dn, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_mxfp8(qg, sg, wq_dn, ws_dn, None,
-                                                                          None, y))
-    mxq = lambda m, k: 3 * m * k + m * k // 32  # noqa: E731  (2 B in, 1 B code, 1/32 B scale)
+    ms_qx, _ = time_calls(torch, stream, lambda: quant(x, qx, sx))
+    ms_up, _ = time_calls(torch, stream, lambda: mm(qx, sx, wq_up, ws_up, None, "gelu_tanh", g))
+    ms_qg, _ = time_calls(torch, stream, lambda: quant(g, qg, sg))
+    ms_dn, _ = time_calls(torch, stream, lambda: mm(qg, sg, wq_dn, ws_dn, None, None, y))
+    # 2 B in, then 1 B (MXFP8) or 1/2 B (MXFP4) of code and 1/32 B of scale per element
+    mxq = lambda m, k: 2 * m * k + m * k * bits // 8 + m * k // 32  # noqa: E731
     fl = 2.0 * M * N * K
     out["quant_x"] = {"ms": ms_qx, "gbs": mxq(M, K) / ms_qx / 1e6}
     out["gemm_up_gelu"] = {"ms": ms_up, "tflops": fl / ms_up / 1e9,
-                           "frac_fp8_peak": fl / ms_up / 1e9 / FP8_PEAK_TFLOPS}
+                           "frac_peak": fl / ms_up / 1e9 / peak}
     out["quant_g"] = {"ms": ms_qg, "gbs": mxq(M, N) / ms_qg / 1e6}
     out["gemm_down"] = {"ms": ms_dn, "tflops": 2.0 * M * N2 * N / ms_dn / 1e9,
-                        "frac_fp8_peak": 2.0 * M * N2 * N / ms_dn / 1e9 / FP8_PEAK_TFLOPS}
+                        "frac_peak": 2.0 * M * N2 * N / ms_dn / 1e9 / peak}
     step = ms_qx + ms_up + ms_qg + ms_dn
     out["step_ms_sum_of_medians"] = step
     out["step_tflops"] = 4.0 * M * N * K / step / 1e9
@@ -422,7 +428,9 @@ def main():
 
     ext = {}
     if not args.no_extras:
-        ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y)
+        ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 8)
+        torch.cuda.synchronize()
+        ext["c4_mxfp4_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 4)
         torch.cuda.synchronize()
         del x, g, qg, y, qx
         torch.cuda.empty_cache()
