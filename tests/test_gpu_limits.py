@@ -1,0 +1,78 @@
+"""GEMMs at the largest K each entry point accepts, so that every 32-bit
+buffer offset and record count runs at its bound: FP8 on both kernels
+(K = 2^22), MXFP8 (K = 2^22) and MXFP4 (K = 2^23).  Codes are random on the
+device; outputs are checked on sampled rows x columns against the oracle
+(which takes the matching rows of the operands).  MX scales change with the
+K block (a different power of two every block), so a misplaced scale word
+at a large offset would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from gpu_util import assert_fp8_tolerance, host_bits, mx_grouped, needs_gpu, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+@pytest.fixture(scope="module")
+def tfq():
+    import int8_w8a8_quantized_amd as m
+
+    return m
+
+
+def _codes(g, rows, cols, fp4=False):
+    t = torch.randint(0, 256, (rows, cols), dtype=torch.uint8, device="cuda", generator=g)
+    if not fp4:
+        t[(t & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    return t
+
+
+ROWS = np.array([0, 1, 97, 255])
+
+
+@pytest.mark.parametrize("M,N", [(2048, 2048), (264, 264)])
+def test_fp8_max_k(tfq, M, N):
+    K = 1 << 22
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a, b = _codes(g, M, K), _codes(g, N, K)
+    sa = torch.rand((M,), device="cuda", generator=g) * 1e-3
+    sb = torch.rand((N,), device="cuda", generator=g) * 1e-3
+    say(f"fp8 max K: M={M} N={N} K={K}")
+    y = tfq.tfq_scaled_mm_fp8(a, sa, b, sb)
+    torch.cuda.synchronize()
+    cols = np.array([0, 5, 130, N - 1])
+    r, c = torch.from_numpy(ROWS), torch.from_numpy(cols)
+    ref = orc.linear_ref(host_bits(a[r]), host_bits(sa[r]), host_bits(b[c]), host_bits(sb[c]),
+                         "fp8")
+    assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, f"fp8 max K {M}x{N}")
+
+
+def _mx_scale_row(K):
+    """One row of E8M0 scales [K/32] that differ per K block: 120 + (block % 15)."""
+    return (120 + np.arange(K // 32) % 15).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_mx_max_k(tfq, fp4):
+    M, N = 512, 264
+    K = (1 << 23) if fp4 else (1 << 22)
+    kb = K // 2 if fp4 else K
+    g = torch.Generator(device="cuda").manual_seed(2)
+    a, b = _codes(g, M, kb, fp4), _codes(g, N, kb, fp4)
+    row = _mx_scale_row(K)
+    grouped_row = torch.from_numpy(mx_grouped(row[None, :])).cuda()   # [K/128, 1, 4]
+    sa = grouped_row.expand(K // 128, M, 4).contiguous()
+    sb = grouped_row.expand(K // 128, N, 4).contiguous()
+    say(f"mx max K: fp4={fp4} M={M} N={N} K={K}")
+    mm = tfq.tfq_scaled_mm_mxfp4 if fp4 else tfq.tfq_scaled_mm_mxfp8
+    y = mm(a, sa, b, sb)
+    torch.cuda.synchronize()
+    cols = np.array([0, 7, 200, N - 1])
+    ref_fn = orc.linear_mx4_ref if fp4 else orc.linear_mx_ref
+    r, c = torch.from_numpy(ROWS), torch.from_numpy(cols)
+    ref = ref_fn(host_bits(a[r]), np.repeat(row[None, :], ROWS.size, 0), host_bits(b[c]),
+                 np.repeat(row[None, :], cols.size, 0))
+    assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, f"mx max K fp4={fp4}")
