@@ -304,7 +304,13 @@ class QuantLinear:
     """W8A8 Linear holding a BF16 weight [out, in]: the weight is quantised per
     output channel (or per 128x128 block) on the first call and kept resident,
     activations are quantised per token (or per 1x128 group) on every call
-    (TeleFuser "Quantization", "tf-kernel FP8: online W8A8")."""
+    (TeleFuser "Quantization", "tf-kernel FP8: online W8A8").  qtype "mxfp8"
+    or "mxfp4" uses the MX formats instead (32-element blocks with E8M0
+    scales, weight and activations alike; TeleFuser "Quantization",
+    converter section)."""
+
+    MX = {"mxfp8": (tfq_quantize_mx, tfq_scaled_mm_mxfp8),
+          "mxfp4": (tfq_quantize_mxfp4, tfq_scaled_mm_mxfp4)}
 
     def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, qtype="fp8",
                  act_qmax: float | None = None, weight_qmax: float | None = None,
@@ -312,7 +318,8 @@ class QuantLinear:
         self.weight = weight
         self.bias = bias
         self.qtype = qtype
-        default = 448.0 if _qt(qtype) == 0 else 127.0
+        self.mx = self.MX.get(qtype) if isinstance(qtype, str) else None
+        default = 448.0 if self.mx or _qt(qtype) == 0 else 127.0
         self.act_qmax = default if act_qmax is None else act_qmax
         self.weight_qmax = default if weight_qmax is None else weight_qmax
         self.scale_block = scale_block
@@ -320,15 +327,26 @@ class QuantLinear:
         self.w_q = None
         self.w_scale = None
         self._ws = None
+        self._act = None
 
     def quantized_weight(self):
         if self.w_q is None:
-            self.w_q, self.w_scale = tfq_quantize_weight_per_channel(
-                self.weight, self.qtype, self.weight_qmax, self.scale_block)
+            if self.mx:
+                self.w_q, self.w_scale = self.mx[0](self.weight)
+            else:
+                self.w_q, self.w_scale = tfq_quantize_weight_per_channel(
+                    self.weight, self.qtype, self.weight_qmax, self.scale_block)
         return self.w_q, self.w_scale
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
         w_q, w_s = self.quantized_weight()
+        if self.mx:
+            quant, mm = self.mx
+            if self._act is None or self._act[0].shape[0] != x.shape[0]:
+                self._act = quant(x)
+            else:
+                quant(x, *self._act)
+            return mm(self._act[0], self._act[1], w_q, w_s, self.bias, self.epi, y)
         need = tfq_quant_linear_workspace_bytes(x.shape[0], x.shape[1], self.qtype,
                                                 self.scale_block)
         if self._ws is None or self._ws.numel() < need:

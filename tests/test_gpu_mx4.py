@@ -145,3 +145,27 @@ def test_mxfp4_big_shape_sampled_rows(tfq):
                                      rng.choice(np.arange(8, M - 8), 16, replace=False)]))
     ref = orc.linear_mx4_ref(qa, sa, qb, sb, rows=rows)
     assert_fp8_tolerance(host_bits(y)[rows], ref, "mx4 big")
+
+
+@pytest.mark.parametrize("qtype", ["mxfp8", "mxfp4"])
+def test_quant_linear_mx_modes(tfq, qtype):
+    """QuantLinear in the MX modes equals quantise + GEMM through the entry
+    points, and keeps its quantised weight."""
+    M, N, K = 200, 264, 512
+    rng = np.random.default_rng(4)
+    xb = _blocky(rng, M, K)
+    wb = _blocky(rng, N, K, sigma=0.02, spread=3)
+    bias = synth.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    say(f"QuantLinear {qtype} M={M} N={N} K={K}")
+    lin = tfq.QuantLinear(dev_bf16(wb), dev_bf16(bias), qtype=qtype, epi="gelu_tanh")
+    y1 = lin(dev_bf16(xb))
+    wq = lin.w_q
+    y2 = lin(dev_bf16(xb))
+    quant = tfq.tfq_quantize_mx if qtype == "mxfp8" else tfq.tfq_quantize_mxfp4
+    mm = tfq.tfq_scaled_mm_mxfp8 if qtype == "mxfp8" else tfq.tfq_scaled_mm_mxfp4
+    qa, sa = quant(dev_bf16(xb))
+    qb, sb = quant(dev_bf16(wb))
+    y3 = mm(qa, sa, qb, sb, dev_bf16(bias), "gelu_tanh")
+    torch.cuda.synchronize()
+    assert lin.w_q is wq
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
