@@ -84,6 +84,17 @@ def lib():
         L.tfq_oracle_quantize_mx.argtypes = [P, i64, i64, i64, P, P]
         L.tfq_oracle_linear_mx_ref.restype = None
         L.tfq_oracle_linear_mx_ref.argtypes = [P, P, P, P, i64, i64, i64, P, ctypes.c_int, P, i64, P]
+        L.tfq_oracle_fp6_value.restype = ctypes.c_double
+        L.tfq_oracle_fp6_value.argtypes = [ctypes.c_int, ctypes.c_uint8]
+        L.tfq_oracle_fp6_encode.restype = ctypes.c_uint8
+        L.tfq_oracle_fp6_encode.argtypes = [ctypes.c_int, ctypes.c_float]
+        L.tfq_oracle_mx6_scale_code.restype = ctypes.c_uint8
+        L.tfq_oracle_mx6_scale_code.argtypes = [ctypes.c_int, ctypes.c_float]
+        L.tfq_oracle_quantize_mx6.restype = None
+        L.tfq_oracle_quantize_mx6.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P]
+        L.tfq_oracle_linear_mx6_ref.restype = None
+        L.tfq_oracle_linear_mx6_ref.argtypes = [ctypes.c_int, P, P, P, P, i64, i64, i64, P,
+                                                ctypes.c_int, P, i64, P]
         L.tfq_oracle_e2m1_value.restype = ctypes.c_double
         L.tfq_oracle_e2m1_value.argtypes = [ctypes.c_uint8]
         L.tfq_oracle_e2m1_encode.restype = ctypes.c_uint8
@@ -429,6 +440,59 @@ def linear_mx4_ref(a_q, a_scale, b_q, b_scale, bias=None, gelu: bool = False,
     out = np.empty((R, N), dtype=np.float64)
     lib().tfq_oracle_linear_mx4_ref(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(bi),
                                     1 if gelu else 0, _ptr(r), nr, _ptr(out))
+    return out
+
+
+FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
+
+
+def _fp6(fmt) -> int:
+    return FP6_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def fp6_value(fmt, code: int) -> float:
+    """Value of a 6-bit E2M3 / E3M2 code (sign in bit 5)."""
+    return lib().tfq_oracle_fp6_value(_fp6(fmt), code)
+
+
+def fp6_encode(fmt, v: float) -> int:
+    return int(lib().tfq_oracle_fp6_encode(_fp6(fmt), v))
+
+
+def mx6_scale_code(fmt, amax: float) -> int:
+    return int(lib().tfq_oracle_mx6_scale_code(_fp6(fmt), float(amax)))
+
+
+def quantize_mx6(x_bf16: np.ndarray, fmt):
+    """MXFP6 quantisation of BF16 rows: (codes uint8 [R, 3C/4], a little-endian
+    6-bit stream per row; E8M0 scales uint8 [R, C/32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    R, C = x.shape
+    assert C % 32 == 0
+    q = np.empty((R, C * 3 // 4), dtype=np.uint8)
+    s = np.empty((R, C // 32), dtype=np.uint8)
+    lib().tfq_oracle_quantize_mx6(_fp6(fmt), _ptr(x), R, C, C, _ptr(q), _ptr(s))
+    return q, s
+
+
+def linear_mx6_ref(a_q, a_scale, b_q, b_scale, fmt, bias=None, gelu: bool = False,
+                   rows=None) -> np.ndarray:
+    """MXFP6 Linear reference y [R, N] in binary64."""
+    a = np.ascontiguousarray(a_q, dtype=np.uint8)
+    b = np.ascontiguousarray(b_q, dtype=np.uint8)
+    M, KB = a.shape
+    N = b.shape[0]
+    K = KB * 4 // 3
+    assert b.shape[1] == KB and K % 32 == 0
+    sa = np.ascontiguousarray(a_scale, dtype=np.uint8)
+    sb = np.ascontiguousarray(b_scale, dtype=np.uint8)
+    assert sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    r, nr = _rows_arg(rows)
+    R = M if r is None else nr
+    out = np.empty((R, N), dtype=np.float64)
+    lib().tfq_oracle_linear_mx6_ref(_fp6(fmt), _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K,
+                                    _ptr(bi), 1 if gelu else 0, _ptr(r), nr, _ptr(out))
     return out
 
 

@@ -545,6 +545,140 @@ void tfq_oracle_linear_mx4_ref(const uint8_t* a, const uint8_t* a_scale, const u
     }
 }
 
+/* ---- MXFP6 ----
+ * OCP MX v1.0 with FP6 elements: E2M3 (1 sign, 2 exponent bits with bias 1,
+ * 3 mantissa bits; largest 7.5 = 1.875 * 2^2) or E3M2 (3 exponent bits with
+ * bias 3, 2 mantissa bits; largest 28 = 1.75 * 2^4), no infinities or NaN.
+ * Shared exponent floor(log2(amax)) - emax (2 for E2M3, 4 for E3M2); the
+ * elements are rounded to the nearest value, ties to the even code, clamped
+ * at the largest.  Six-bit codes are packed as a little-endian bit stream:
+ * element i of a row takes bits 6 i .. 6 i + 5 of the row's bytes (four
+ * elements per three bytes). */
+static void fp6_params(int fmt, int* ebits, int* mbits, int* bias)
+{
+    if (fmt == 0) { *ebits = 2; *mbits = 3; *bias = 1; }   /* E2M3 */
+    else { *ebits = 3; *mbits = 2; *bias = 3; }             /* E3M2 */
+}
+
+/* Value of a 6-bit code (sign in bit 5). */
+double tfq_oracle_fp6_value(int fmt, uint8_t code)
+{
+    int eb, mb, bias;
+    fp6_params(fmt, &eb, &mb, &bias);
+    const int e = (code >> mb) & ((1 << eb) - 1);
+    const int m = code & ((1 << mb) - 1);
+    double v = e == 0 ? ldexp((double)m, 1 - bias - mb)
+                      : ldexp(1.0 + ldexp((double)m, -mb), e - bias);
+    return (code & 32) ? -v : v;
+}
+
+/* Nearest FP6 code of t, searched over all 32 magnitudes (saturating at the
+ * largest; ties to the even code; sign kept, also for zero). */
+uint8_t tfq_oracle_fp6_encode(int fmt, float t)
+{
+    const int neg = signbit(t) != 0;
+    const double a = fabs((double)t);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 32; ++c) {
+        const double d = fabs(a - tfq_oracle_fp6_value(fmt, (uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (uint8_t)(best | (neg ? 32 : 0));
+}
+
+uint8_t tfq_oracle_mx6_scale_code(int fmt, float amax)
+{
+    int e;
+    if (!(amax > 0.0f)) return 0;
+    (void)frexpf(amax, &e);
+    int shared = (e - 1) - (fmt == 0 ? 2 : 4);
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
+static void put6(uint8_t* row, int64_t i, uint8_t code)
+{
+    const int64_t bit = 6 * i;
+    const uint32_t v = (uint32_t)(code & 63) << (bit & 7);
+    row[bit >> 3] |= (uint8_t)v;
+    if ((bit & 7) > 2) row[(bit >> 3) + 1] |= (uint8_t)(v >> 8);
+}
+
+static uint8_t get6(const uint8_t* row, int64_t i)
+{
+    const int64_t bit = 6 * i;
+    uint32_t v = row[bit >> 3];
+    if ((bit & 7) > 2) v |= (uint32_t)row[(bit >> 3) + 1] << 8;
+    return (uint8_t)((v >> (bit & 7)) & 63);
+}
+
+/* Quantise rows of BF16 x [rows, cols] (cols % 32 == 0) to MXFP6: packed
+ * codes [rows, 3 cols / 4] bytes and E8M0 scales [rows, cols / 32]. */
+void tfq_oracle_quantize_mx6(int fmt, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                             uint8_t* q, uint8_t* scale)
+{
+    const int64_t nb = cols / 32, rb = cols * 3 / 4;
+    int eb, mb, bias;
+    fp6_params(fmt, &eb, &mb, &bias);
+    const float maxv = (float)tfq_oracle_fp6_value(fmt, 31);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        uint8_t* qr = q + r * rb;
+        for (int64_t i = 0; i < rb; ++i) qr[i] = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + r * ld + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(tfq_oracle_bf16_to_f32(xb[i]));
+                if (a > amax) amax = a;
+            }
+            const uint8_t code = tfq_oracle_mx6_scale_code(fmt, amax);
+            scale[r * nb + b] = code;
+            const double X = ldexp(1.0, (int)code - 127);
+            for (int i = 0; i < 32; ++i) {
+                float t = (float)((double)tfq_oracle_bf16_to_f32(xb[i]) / X);
+                t = fminf(fmaxf(t, -maxv), maxv);
+                put6(qr, b * 32 + i, tfq_oracle_fp6_encode(fmt, t));
+            }
+        }
+    }
+}
+
+/* MXFP6 Linear reference in binary64 for selected rows. */
+void tfq_oracle_linear_mx6_ref(int fmt, const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                               const uint8_t* b_scale, int64_t M, int64_t N, int64_t K,
+                               const uint16_t* bias, int epi, const int64_t* rows, int64_t nrows,
+                               double* y)
+{
+    const int64_t R = rows ? nrows : M;
+    const int64_t nb = K / 32, rb = K * 3 / 4;
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < R; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+        for (int64_t k = 0; k < K; ++k) arow[k] = tfq_oracle_fp6_value(fmt, get6(a + m * rb, k));
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            for (int64_t kb = 0; kb < nb; ++kb) {
+                double acc = 0.0;
+                for (int64_t k = kb * 32; k < kb * 32 + 32; ++k)
+                    acc += arow[k] * tfq_oracle_fp6_value(fmt, get6(b + n * rb, k));
+                v += ldexp(acc, (int)a_scale[m * nb + kb] - 127 + (int)b_scale[n * nb + kb] - 127);
+            }
+            if (bias) v += (double)tfq_oracle_bf16_to_f32(bias[n]);
+            if (epi == 1) v = tfq_oracle_gelu_tanh(v);
+            y[i * N + n] = v;
+        }
+        free(arow);
+    }
+}
+
 /* INT8 W8A8: exact INT32 accumulators (held in int64 here; the caller keeps
  * K small enough that they fit INT32) and the fixed-order BF16 output.
  * acc and y_bf16 may each be NULL. */
