@@ -176,14 +176,16 @@ FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (and FP6) MFMA
 
 
 def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, bits=8):
-    """The same FFN pair in MXFP8 (bits 8) or MXFP4 (bits 4): E8M0 scale per
-    32 elements, scales applied by the scaled MFMA; each call timed on its
-    own (median of 20)."""
+    """The same FFN pair in MXFP8 (bits 8), MXFP6 with E2M3 elements (bits 6)
+    or MXFP4 (bits 4): E8M0 scale per 32 elements, scales applied by the
+    scaled MFMA; each call timed on its own (median of 20)."""
     log(f"extras: c4 FFN pair in MXFP{bits}")
     M, K = x.shape
     N, N2 = w_up.shape[0], w_dn.shape[0]
-    quant = tfq.tfq_quantize_mx if bits == 8 else tfq.tfq_quantize_mxfp4
-    mm = tfq.tfq_scaled_mm_mxfp8 if bits == 8 else tfq.tfq_scaled_mm_mxfp4
+    quant = {8: tfq.tfq_quantize_mx, 4: tfq.tfq_quantize_mxfp4,
+             6: lambda t, *o: tfq.tfq_quantize_mxfp6(t, "e2m3", *o)}[bits]
+    mm = {8: tfq.tfq_scaled_mm_mxfp8, 4: tfq.tfq_scaled_mm_mxfp4,
+          6: lambda *a: tfq.tfq_scaled_mm_mxfp6(*a[:4], "e2m3", *a[4:])}[bits]
     peak = FP8_PEAK_TFLOPS if bits == 8 else FP4_PEAK_TFLOPS
     wq_up, ws_up = quant(w_up)
     wq_dn, ws_dn = quant(w_dn)
@@ -194,7 +196,8 @@ def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, bits=8):
     ms_up, _ = time_calls(torch, stream, lambda: mm(qx, sx, wq_up, ws_up, None, "gelu_tanh", g))
     ms_qg, _ = time_calls(torch, stream, lambda: quant(g, qg, sg))
     ms_dn, _ = time_calls(torch, stream, lambda: mm(qg, sg, wq_dn, ws_dn, None, None, y))
-    # 2 B in, then 1 B (MXFP8) or 1/2 B (MXFP4) of code and 1/32 B of scale per element
+    # 2 B in, then 1 B (MXFP8), 3/4 B (MXFP6) or 1/2 B (MXFP4) of code and
+    # 1/32 B of scale per element
     mxq = lambda m, k: 2 * m * k + m * k * bits // 8 + m * k // 32  # noqa: E731
     fl = 2.0 * M * N * K
     out["quant_x"] = {"ms": ms_qx, "gbs": mxq(M, K) / ms_qx / 1e6}
@@ -429,6 +432,8 @@ def main():
     ext = {}
     if not args.no_extras:
         ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 8)
+        torch.cuda.synchronize()
+        ext["c4_mxfp6_e2m3_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 6)
         torch.cuda.synchronize()
         ext["c4_mxfp4_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 4)
         torch.cuda.synchronize()

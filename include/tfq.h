@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 6
+#define TFQ_ABI_VERSION 7
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -322,6 +322,37 @@ tfq_status tfq_scaled_mm_mxfp4(const uint8_t* a_q, const uint32_t* a_scale, cons
                                const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
 
 /*
+ * MXFP6 quantisation: 6-bit codes with one E8M0 scale byte per 32
+ * consecutive elements of a row.  TeleFuser "Quantization", converter
+ * section (MXFP6 uses 32-value blocks with E8M0 scales); OCP MX v1.0.
+ *   fmt 0: E2M3 (2 exponent bits with bias 1, 3 mantissa bits, largest 7.5,
+ *          shared exponent floor(log2(amax)) - 2);
+ *   fmt 1: E3M2 (3 exponent bits with bias 3, 2 mantissa bits, largest 28,
+ *          shared exponent floor(log2(amax)) - 4).
+ * Scale byte = shared + 127 (clamped to [0, 254]); codes = nearest value of
+ * x * 2^-shared clamped to the largest, ties to the even code, sign in bit 5
+ * (kept for zero).
+ *   q_out     [rows, 3 cols / 4] bytes: per row a little-endian bit stream,
+ *             element i in bits 6 i .. 6 i + 5; 16-byte aligned.
+ *   scale_out [cols/128, rows] scale words as for tfq_quantize_mx.
+ *   rows >= 1; cols >= 128, cols % 128 == 0; rows * cols / 32 <= 2^30.
+ */
+tfq_status tfq_quantize_mxfp6(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              int32_t fmt, void* q_out, uint32_t* scale_out, void* stream);
+
+/*
+ * MXFP6 GEMM, as tfq_scaled_mm_mxfp8 over 6-bit codes of format fmt (both
+ * operands): a_q [m, 3k/4], b_q [n, 3k/4] as tfq_quantize_mxfp6 writes them,
+ * a_scale [k/128, m], b_scale [k/128, n] scale words.  TeleFuser
+ * "Quantization", converter section (MXFP6 block format).
+ *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 4194304, k % 128 == 0;
+ *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
+ */
+tfq_status tfq_scaled_mm_mxfp6(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
+                               const uint32_t* b_scale, int64_t m, int64_t n, int64_t k, int32_t fmt,
+                               const void* bias_bf16, int32_t epi, void* y_bf16, void* stream);
+
+/*
  * FP8 KV cache.  TeleFuser "Quantization", "Other quantized data paths"
  * (LiveAct FP8 KV cache: K/V stored as E4M3FN with one FP32 scale per
  * last-dimension vector, dequantised to the requested attention dtype on
@@ -379,7 +410,8 @@ tfq_status tfq_set_autotune(int32_t mode);
  * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU) and band (tile rows per
  * band of the tile order), else 0.  kind: 0 FP8 per channel
  * (tfq_scaled_mm_fp8, scale_block 0, and the fused FP8 Linear), 1 INT8,
- * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4.  Looks up the
+ * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4,
+ * 6 MXFP6 E2M3, 7 MXFP6 E3M2.  Looks up the
  * current device's entries.
  */
 int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,

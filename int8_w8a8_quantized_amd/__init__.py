@@ -25,7 +25,8 @@ __all__ = [
     "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
     "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
     "tfq_kv_cache_load", "KV_DTYPE", "tfq_set_autotune", "tfq_autotune_lookup",
-    "tfq_autotune_clear", "tfq_quantize_mxfp4", "tfq_scaled_mm_mxfp4",
+    "tfq_autotune_clear", "tfq_quantize_mxfp4", "tfq_scaled_mm_mxfp4", "tfq_quantize_mxfp6",
+    "tfq_scaled_mm_mxfp6", "FP6",
     "tfq_abi_version", "QuantLinear",
 ]
 
@@ -247,7 +248,9 @@ def tfq_set_autotune(mode: int) -> None:
     check(lib().tfq_set_autotune(int(mode)), "tfq_set_autotune")
 
 
-AUTOTUNE_KIND = {"fp8": 0, "int8": 1, "fp8_block": 2, "mxfp8": 3, "grouped_fp8": 4, "mxfp4": 5}
+AUTOTUNE_KIND = {"fp8": 0, "int8": 1, "fp8_block": 2, "mxfp8": 3, "grouped_fp8": 4, "mxfp4": 5,
+                 "mxfp6_e2m3": 6, "mxfp6_e3m2": 7}
+FP6 = {"e2m3": 0, "e3m2": 1}
 
 
 def tfq_autotune_lookup(kind, m: int, n: int, k: int, epi=None, groups: int = 0):
@@ -291,6 +294,33 @@ def tfq_scaled_mm_mxfp4(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None,
     return y
 
 
+def tfq_quantize_mxfp6(x: torch.Tensor, fmt="e2m3", q_out=None, scale_out=None, stream=None):
+    """MXFP6 quantisation of BF16 rows x [rows, cols] (fmt "e2m3" or "e3m2"):
+    returns (codes uint8 [rows, 3 cols / 4], a 6-bit little-endian stream per
+    row; E8M0 scales uint8 [cols/128, rows, 4] as tfq_quantize_mx)."""
+    rows, cols = x.shape
+    if q_out is None:
+        q_out = torch.empty((rows, cols // 4 * 3), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=x.device)
+    check(lib().tfq_quantize_mxfp6(_ptr(x), rows, cols, x.stride(0), FP6[fmt], _ptr(q_out),
+                                   _ptr(scale_out), _stream(stream)), "tfq_quantize_mxfp6")
+    return q_out, scale_out
+
+
+def tfq_scaled_mm_mxfp6(a_q, a_scale, b_q, b_scale, fmt="e2m3", bias=None, epi=None, y=None,
+                        stream=None):
+    """y [m, n] BF16 from MXFP6 operands a_q [m, 3k/4], b_q [n, 3k/4]."""
+    m, kb = a_q.shape
+    n = b_q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    check(lib().tfq_scaled_mm_mxfp6(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n,
+                                    kb // 3 * 4, FP6[fmt], _ptr(bias), _epi(epi), _ptr(y),
+                                    _stream(stream)), "tfq_scaled_mm_mxfp6")
+    return y
+
+
 def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):
     """The device's E4M3FN encoder over a float32 tensor (numel % 4 == 0)."""
     if q is None:
@@ -304,13 +334,17 @@ class QuantLinear:
     """W8A8 Linear holding a BF16 weight [out, in]: the weight is quantised per
     output channel (or per 128x128 block) on the first call and kept resident,
     activations are quantised per token (or per 1x128 group) on every call
-    (TeleFuser "Quantization", "tf-kernel FP8: online W8A8").  qtype "mxfp8"
-    or "mxfp4" uses the MX formats instead (32-element blocks with E8M0
-    scales, weight and activations alike; TeleFuser "Quantization",
-    converter section)."""
+    (TeleFuser "Quantization", "tf-kernel FP8: online W8A8").  qtype "mxfp8",
+    "mxfp6_e2m3", "mxfp6_e3m2" or "mxfp4" uses the MX formats instead
+    (32-element blocks with E8M0 scales, weight and activations alike;
+    TeleFuser "Quantization", converter section)."""
 
     MX = {"mxfp8": (tfq_quantize_mx, tfq_scaled_mm_mxfp8),
-          "mxfp4": (tfq_quantize_mxfp4, tfq_scaled_mm_mxfp4)}
+          "mxfp4": (tfq_quantize_mxfp4, tfq_scaled_mm_mxfp4),
+          "mxfp6_e2m3": (lambda x, *o: tfq_quantize_mxfp6(x, "e2m3", *o),
+                         lambda *a: tfq_scaled_mm_mxfp6(*a[:4], "e2m3", *a[4:])),
+          "mxfp6_e3m2": (lambda x, *o: tfq_quantize_mxfp6(x, "e3m2", *o),
+                         lambda *a: tfq_scaled_mm_mxfp6(*a[:4], "e3m2", *a[4:]))}
 
     def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None, qtype="fp8",
                  act_qmax: float | None = None, weight_qmax: float | None = None,

@@ -45,6 +45,8 @@ SIGNATURES = [
     ("tfq_scaled_mm_mxfp8", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _P]),
     ("tfq_quantize_mxfp4", _I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     ("tfq_scaled_mm_mxfp4", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _P]),
+    ("tfq_quantize_mxfp6", _I32, [_P, _I64, _I64, _I64, _I32, _P, _P, _P]),
+    ("tfq_scaled_mm_mxfp6", _I32, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _I32, _P, _P]),
     ("tfq_kv_cache_store", _I32, [_P, _I64, _I64, _I64, _I64, _P, _I64, _F, _P, _P, _P]),
     ("tfq_kv_cache_load", _I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _I32, _P, _P]),
     ("tfq_set_autotune", _I32, [_I32]),

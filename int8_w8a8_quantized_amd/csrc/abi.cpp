@@ -406,6 +406,53 @@ tfq_status tfq_scaled_mm_mxfp4(const uint8_t* a_q, const uint32_t* a_scale, cons
     return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
 }
 
+tfq_status tfq_quantize_mxfp6(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              int32_t fmt, void* q_out, uint32_t* scale_out, void* stream)
+{
+    if (!x_bf16 || !q_out || !scale_out) return TFQ_ERR_NULL_POINTER;
+    if (fmt != 0 && fmt != 1) return TFQ_ERR_UNSUPPORTED;
+    if (rows < 1 || rows > kMaxDim || cols < 128 || cols > kMaxDim || cols % 128 != 0 ||
+        ld_x < cols || ld_x > kMaxDim || !mx_scales_fit(rows, cols))
+        return TFQ_ERR_BAD_SHAPE;
+    if (ld_x % 8 != 0 || !aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(scale_out, 4))
+        return TFQ_ERR_MISALIGNED;
+    const Range rx = range_of(x_bf16, ((rows - 1) * ld_x + cols) * 2);
+    const Range rq = range_of(q_out, rows * (cols / 4 * 3)), rs = range_of(scale_out, rows * (cols / 32));
+    if (overlap(rx, rq) || overlap(rx, rs) || overlap(rq, rs)) return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    return hip_status(tfq::launch_quantize_mx((const uint16_t*)x_bf16, rows, cols, ld_x,
+                                              (uint8_t*)q_out, scale_out, (hipStream_t)stream,
+                                              fmt == 0 ? 62 : 63));
+}
+
+tfq_status tfq_scaled_mm_mxfp6(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
+                               const uint32_t* b_scale, int64_t m, int64_t n, int64_t k, int32_t fmt,
+                               const void* bias_bf16, int32_t epi, void* y_bf16, void* stream)
+{
+    if (!a_q || !a_scale || !b_q || !b_scale || !y_bf16) return TFQ_ERR_NULL_POINTER;
+    if (!epi_ok(epi) || (fmt != 0 && fmt != 1)) return TFQ_ERR_UNSUPPORTED;
+    if (m < 1 || m > kMaxDim || n < 8 || n > kMaxDim || n % 8 != 0 || k < 128 ||
+        k > ((int64_t)1 << 22) || k % 128 != 0 || !mx_scales_fit(m, k) || !mx_scales_fit(n, k))
+        return TFQ_ERR_BAD_SHAPE;
+    if (((m + 255) / 256) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
+        (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        return TFQ_ERR_MISALIGNED;
+    const Range ry = range_of(y_bf16, m * n * 2);
+    const Range ins[5] = {range_of(a_q, m * (k / 4 * 3)), range_of(b_q, n * (k / 4 * 3)),
+                          range_of(a_scale, m * (k / 32)), range_of(b_scale, n * (k / 32)),
+                          range_of(bias_bf16, bias_bf16 ? n * 2 : 0)};
+    for (const Range& r : ins)
+        if (overlap(r, ry)) return TFQ_ERR_ALIAS;
+    tfq_status st = check_device();
+    if (st != TFQ_OK) return st;
+    tfq::GemmArgs g{a_q, b_q, nullptr, nullptr, (const uint16_t*)bias_bf16, (uint16_t*)y_bf16,
+                    nullptr, m, n, k, fmt == 0 ? tfq::kMxE2M3 : tfq::kMxE3M2, 0, epi, a_scale,
+                    b_scale};
+    return hip_status(tfq::launch_scaled_gemm(g, (hipStream_t)stream));
+}
+
 tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, const uint8_t* b_q,
                                const uint32_t* b_scale, int64_t m, int64_t n, int64_t k,
                                const void* bias_bf16, int32_t epi, void* y_bf16, void* stream)
@@ -505,6 +552,8 @@ int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32
     case 2: g.qtype = tfq::kE4M3FN; g.scale_block = 128; break;
     case 3: g.qtype = tfq::kMxE4M3; break;
     case 5: g.qtype = tfq::kMxE2M1; break;
+    case 6: g.qtype = tfq::kMxE2M3; break;
+    case 7: g.qtype = tfq::kMxE3M2; break;
     case 4: g.qtype = tfq::kE4M3FN; g.groups = groups; break;
     default: return 0;
     }

@@ -43,6 +43,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
@@ -208,6 +209,14 @@ template <>
 struct PipeAcc<kMxE2M1> {
     typedef v16f type;
 };
+template <>
+struct PipeAcc<kMxE2M3> {
+    typedef v16f type;
+};
+template <>
+struct PipeAcc<kMxE3M2> {
+    typedef v16f type;
+};
 
 template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -216,6 +225,10 @@ void gemm_pipe_kernel(const Params p)
     // MXFP4 rows hold two codes per byte: K counts bytes below, and a stage
     // (128 bytes) holds 256 elements = two 128-element scale groups
     constexpr bool FP4 = QT == kMxE2M1;
+    // MXFP6 rows hold 3 bytes per 4 codes: a stage is 128 elements = 96
+    // bytes, loaded into 128-byte LDS rows whose chunks 6 and 7 stay zero
+    constexpr bool FP6 = QT == kMxE2M3 || QT == kMxE3M2;
+    constexpr int SK = FP6 ? 96 : PK;  // K bytes per stage
     __shared__ __attribute__((aligned(16))) uint8_t smem[FP4 ? PSMEM + 2 * 2048 : PSMEM];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -287,7 +300,7 @@ void gemm_pipe_kernel(const Params p)
         m0 = tm * BM;
     }
     const int n0 = tn * BN;
-    const int K = FP4 ? p.k / 2 : p.k;
+    const int K = FP4 ? p.k / 2 : FP6 ? p.k / 4 * 3 : p.k;
     const int rows_a = min(BM, m_end - m0), rows_b = min(BN, p.n - n0);
     const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
     const v4i rb = buffer_rsrc(b_grp + (int64_t)n0 * K, rows_b * K);
@@ -326,7 +339,7 @@ void gemm_pipe_kernel(const Params p)
         }
     const int a_rd = wm * 128 * PK;
     const int b_rd = PA + wn * 128 * PK;
-    const int KT = (K + PK - 1) / PK;
+    const int KT = (K + SK - 1) / SK;
 
     typedef typename PipeAcc<QT>::type acc_t;
     acc_t acc[4][4];
@@ -342,10 +355,10 @@ void gemm_pipe_kernel(const Params p)
     // padding stages up to an even count) get bit 31 set in their offset:
     // out of range, they write zeros.
     auto dma = [&](int kt, int ab, int j) {
-        const int k0 = kt * PK;
+        const int k0 = kt * SK;
         const int lc = (j & 1) ? lc_o : lc_e;
-        const int off = (row_off + j * 8 * K + k0 + lc * 16) |
-                        (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+        const bool oob = k0 + lc * 16 >= K || (FP6 && lc >= 6);
+        const int off = (row_off + j * 8 * K + k0 + lc * 16) | (int)((unsigned)oob << 31);
         const uint32_t dst = lds_base + (uint32_t)((kt & 1) * PSTAGE + ab * PA + (8 * wave_u + j) * 1024);
         lds_dma16(ab ? rb : ra, off, dst);
     };
@@ -361,6 +374,34 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
     };
+    // MXFP6: in K step ks lane half h holds the 24 bytes at row byte
+    // 48 ks + 24 h -- one whole 32-element block, in registers 0-5 -- read as
+    // three 8-byte pieces, each inside one (swizzled) 16-byte chunk
+    int rd6[2][3];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+            const int bo = 48 * ks + 24 * h + 8 * pc;
+            rd6[ks][pc] = fr * PK + (((bo >> 4) ^ sw) << 4) + (bo & 15);
+        }
+    auto read6 = [&](int buf, int ks, Frags& f, int q, int pc) {
+        const uint8_t* s = smem + buf * PSTAGE + (q < 4 ? b_rd + q * 32 * PK : a_rd + (q - 4) * 32 * PK);
+        const v2i v = *reinterpret_cast<const v2i*>(s + rd6[ks][pc]);
+        v8i& d = q < 4 ? f.b[q] : f.a[q - 4];
+        d[2 * pc] = v[0];
+        d[2 * pc + 1] = v[1];
+    };
+    // the fragment reads that go with MFMA i of a K step: one 16-byte half
+    // each (16 per K step), or for MXFP6 one or two 8-byte pieces (24)
+    auto read_slots = [&](int buf, int ks, Frags& f, int i) {
+        if constexpr (FP6) {
+#pragma unroll
+            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, sl / 3, sl % 3);
+        } else {
+            read_part(buf, ks, f, i >> 1, i & 1);
+        }
+    };
     // weights as the first operand: the 32x32 result is the transposed
     // output tile, so each lane ends up with 4 consecutive columns
     // MXFP8: the block scales of K step ks are blocks 2 ks (registers 0-3,
@@ -369,7 +410,9 @@ void gemm_pipe_kernel(const Params p)
     // word holds the group's blocks in the byte order 0, 2, 1, 3, so lane
     // half h reads the 16 bits at byte 2 h -- blocks h and 2 + h -- and the
     // MFMA's byte select is ks for every lane (operand order as the data).
-    constexpr bool MX = QT == kMxE4M3 || FP4;
+    constexpr bool MX = QT == kMxE4M3 || FP4 || FP6;
+    // MFMA operand format: 0 E4M3, 2 E2M3, 3 E3M2 (4 E2M1 in the MXFP4 loop)
+    constexpr int FMT = QT == kMxE2M3 ? 2 : QT == kMxE3M2 ? 3 : 0;
     int scA[2][4], scB[2][4];
     auto mfma_one = [&](int mi, int ni, const Frags& f, int set = 0, int ks = 0) {
         if constexpr (QT == kE4M3FN) {
@@ -378,10 +421,10 @@ void gemm_pipe_kernel(const Params p)
         } else if constexpr (MX) {
             if (ks == 0)
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0, scB[set][ni], 0, scA[set][mi]);
+                    f.b[ni], f.a[mi], acc[mi][ni], FMT, FMT, 0, scB[set][ni], 0, scA[set][mi]);
             else
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 1, scB[set][ni], 1, scA[set][mi]);
+                    f.b[ni], f.a[mi], acc[mi][ni], FMT, FMT, 1, scB[set][ni], 1, scA[set][mi]);
         } else {
             const v8i b8 = f.b[ni], a8 = f.a[mi];
             acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
@@ -573,10 +616,7 @@ void gemm_pipe_kernel(const Params p)
         else
             asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            read_part(0, 0, f0, q, 0);
-            read_part(0, 0, f0, q, 1);
-        }
+        for (int i = 0; i < 16; ++i) read_slots(0, 0, f0, i);
         if constexpr (MX) read_mx(0, 0);
 
         for (int kt = 0; kt < KT; kt += 2) {
@@ -587,7 +627,7 @@ void gemm_pipe_kernel(const Params p)
                 for (int i = 0; i < 16; ++i) {
                     mfma_one(i >> 2, i & 3, f0, u, 0);
                     TFQ_FENCE();
-                    read_part(u, 1, f1, i >> 1, i & 1);
+                    read_slots(u, 1, f1, i);
                     TFQ_FENCE();
                 }
                 // own loads of stage kt+u+1 (the only ones in flight) are done
@@ -599,7 +639,7 @@ void gemm_pipe_kernel(const Params p)
                 for (int i = 0; i < 16; ++i) {
                     mfma_one(i >> 2, i & 3, f1, u, 1);
                     TFQ_FENCE();
-                    read_part(u ^ 1, 0, f0, i >> 1, i & 1);
+                    read_slots(u ^ 1, 0, f0, i);
                     if constexpr (MX)
                         if (i == 0) dma_mx(kt + u + 2);
                     dma(kt + u + 2, i & 1, i >> 1);
@@ -1260,6 +1300,12 @@ hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t 
     if (g.qtype == kMxE2M1)
         return g.epi == 1 ? launch_pipe<kMxE2M1, 1, true, false>(p, stream)
                           : launch_pipe<kMxE2M1, 0, true, false>(p, stream);
+    if (g.qtype == kMxE2M3)
+        return g.epi == 1 ? launch_pipe<kMxE2M3, 1, true, false>(p, stream)
+                          : launch_pipe<kMxE2M3, 0, true, false>(p, stream);
+    if (g.qtype == kMxE3M2)
+        return g.epi == 1 ? launch_pipe<kMxE3M2, 1, true, false>(p, stream)
+                          : launch_pipe<kMxE3M2, 0, true, false>(p, stream);
     const bool dual = c.kernel == 1;
     const bool y = g.y != nullptr, a = g.acc != nullptr;
     if (g.qtype == kE4M3FN) {

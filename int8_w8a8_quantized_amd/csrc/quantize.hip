@@ -331,18 +331,45 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float inv)
            (e2m1_code(bf_lo(w.w) * inv) << 24) | (e2m1_code(bf_hi(w.w) * inv) << 28);
 }
 
-template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1)
+// MXFP6 (F == 62: E2M3, bias 1, largest 7.5; F == 63: E3M2, bias 3, largest
+// 28): shared exponent floor(log2(amax)) - emax (2 / 4).  The code of a
+// scaled element t (|t| clamped to the largest value) is
+//   2^mb (e - emin) + rint(|t| 2^(mb - e)),  e = max(floor(log2 |t|), emin),
+// with mb mantissa bits and emin = 1 - bias: rint (ties to even) of the
+// exactly scaled value picks the nearest grid point, the even code on a tie,
+// and a carry into the next binade lands on its first code.  Six-bit codes
+// are a little-endian bit stream per row: a lane's 8 codes are 6 bytes, and
+// lane pairs write their 12 bytes as one aligned store.
+template <int MB, int EMIN>
+__device__ __forceinline__ uint32_t small_float_code(float v, float vmax)
+{
+    const float t = __builtin_fminf(__builtin_fabsf(v), vmax);
+    const int e = max((int)((__float_as_uint(t) >> 23) & 0xFFu) - 127, EMIN);
+    const float up = __uint_as_float((uint32_t)(127 + MB - e) << 23);  // 2^(mb - e)
+    return (uint32_t)((e - EMIN) << MB) + (uint32_t)__builtin_rintf(t * up);
+}
+
+template <int F>
+__device__ __forceinline__ uint32_t fp6_code(float v)
+{
+    constexpr int MB = F == 62 ? 3 : 2, EMIN = F == 62 ? 0 : -2;
+    constexpr float VMAX = F == 62 ? 7.5f : 28.0f;
+    return small_float_code<MB, EMIN>(v, VMAX) | ((__float_as_uint(v) >> 26) & 32u);
+}
+
+template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1), 62 / 63: MXFP6 (E2M3 / E3M2)
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
                                                           int64_t rows, int64_t cols, int64_t ld,
                                                           uint8_t* __restrict__ q,
                                                           uint32_t* __restrict__ scale)
 {
-    constexpr int kEmax = F == 8 ? 8 : 2;  // exponent of the element type's largest normal
+    // exponent of the element type's largest normal
+    constexpr int kEmax = F == 8 ? 8 : F == 63 ? 4 : 2;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
-    uint8_t* qrow = q + row * (F == 8 ? cols : cols / 2);
+    uint8_t* qrow = q + row * (F == 8 ? cols : F == 4 ? cols / 2 : cols / 4 * 3);
     const int nchunk = (int)(cols >> 3);  // a multiple of 16: whole groups only
     constexpr int U = 4;
     for (int base = 0; base < nchunk; base += 64 * U) {
@@ -368,9 +395,26 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
+            if constexpr (F == 62 || F == 63) {
+                // 48-bit code group of this lane, then the pair's 12 bytes
+                const uint4 w = v[u];
+                const uint32_t c0 = fp6_code<F>(bf_lo(w.x) * inv), c1 = fp6_code<F>(bf_hi(w.x) * inv),
+                               c2 = fp6_code<F>(bf_lo(w.y) * inv), c3 = fp6_code<F>(bf_hi(w.y) * inv),
+                               c4 = fp6_code<F>(bf_lo(w.z) * inv), c5 = fp6_code<F>(bf_hi(w.z) * inv),
+                               c6 = fp6_code<F>(bf_lo(w.w) * inv), c7 = fp6_code<F>(bf_hi(w.w) * inv);
+                const uint32_t lo = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18) | (c4 << 24) | (c5 << 30);
+                const uint32_t hi = (c5 >> 2) | (c6 << 4) | (c7 << 10);  // 16 bits
+                const uint32_t plo = (uint32_t)__shfl_xor((int)lo, 1);
+                const uint32_t phi = (uint32_t)__shfl_xor((int)hi, 1);
+                if (idx < nchunk && (lane & 1) == 0)
+                    *reinterpret_cast<uint3*>(qrow + (int64_t)(idx >> 1) * 12) =
+                        make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
+            }
             if (idx < nchunk) {
                 const uint4 w = v[u];
-                if constexpr (F == 8) {
+                if constexpr (F == 62 || F == 63) {
+                    // (stored above)
+                } else if constexpr (F == 8) {
                     uint2 o;
                     o.x = encode4<kE4M3FN>(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv,
                                            bf_hi(w.y) * inv, 448.0f);
@@ -634,6 +678,9 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int
     if (elem_bits == 4)
         hipLaunchKernelGGL((quantize_mx_kernel<4>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
                            rows, cols, ld, q, scale);
+    else if (elem_bits == 62 || elem_bits == 63)
+        hipLaunchKernelGGL((elem_bits == 62 ? quantize_mx_kernel<62> : quantize_mx_kernel<63>),
+                           dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q, scale);
     else
         hipLaunchKernelGGL((quantize_mx_kernel<8>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
                            rows, cols, ld, q, scale);

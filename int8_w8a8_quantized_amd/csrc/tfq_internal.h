@@ -9,8 +9,9 @@
 namespace tfq {
 
 // kMxE4M3: E4M3FN codes with one E8M0 scale per 32 elements along K (MXFP8);
-// kMxE2M1: E2M1 codes, two per byte, with the same scales (MXFP4)
-enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2, kMxE2M1 = 3 };
+// kMxE2M1: E2M1 codes, two per byte, with the same scales (MXFP4);
+// kMxE2M3 / kMxE3M2: 6-bit codes, a little-endian bit stream (MXFP6)
+enum QType : int { kE4M3FN = 0, kInt8 = 1, kMxE4M3 = 2, kMxE2M1 = 3, kMxE2M3 = 4, kMxE3M2 = 5 };
 
 // Launchers enqueue kernels on `stream` and return the launch status.  They
 // assume the arguments already passed the host-side validation.
@@ -25,7 +26,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 
 // MX rows (cols % 128 == 0): E8M0 scale words [cols/128, rows] (bytes 0..3
 // of word (g, r) = blocks 4 g + 0, 2, 1, 3 of row r); elem_bits 8: MXFP8 codes [rows, cols]; 4: MXFP4 codes [rows, cols/2], two
-// per byte (lower index in the low nibble)
+// per byte (lower index in the low nibble); 62 / 63: MXFP6 E2M3 / E3M2 codes
+// [rows, 3 cols / 4], a little-endian 6-bit stream per row
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* q, uint32_t* scale, hipStream_t stream, int elem_bits = 8);
 

@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 6
+    assert L.tfq_abi_version() == 7
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -135,6 +135,18 @@ def test_mx_validation(L):
     assert g(A + 4, B, C, D, 64, 64, 128, None, 0, E, None) == ALIGN
     assert g(A, B, C, D, 64, 64, 128, None, 0, E + 8, None) == ALIGN
     assert g(A, B, C, D, 64, 64, 128, None, 0, B + 16, None) == ALIAS  # y over a_scale
+    q6 = L.tfq_quantize_mxfp6
+    assert q6(A, 4, 128, 128, 0, B, C, None) == DEV
+    assert q6(A, 4, 128, 128, 2, B, C, None) == UNSUP           # format
+    assert q6(A, 4, 160, 160, 1, B, C, None) == SHAPE           # cols % 128
+    assert q6(A, 4, 128, 128, 0, B, B + 380, None) == ALIAS     # scales over the 384 code bytes
+    assert q6(A, 4, 128, 128, 0, B, B + 384, None) == DEV
+    g6 = L.tfq_scaled_mm_mxfp6
+    assert g6(A, B, C, D, 64, 64, 128, 1, None, 0, E, None) == DEV
+    assert g6(A, B, C, D, 64, 64, 128, 3, None, 0, E, None) == UNSUP
+    assert g6(A, B, C, D, 64, 64, 192, 0, None, 0, E, None) == SHAPE
+    assert g6(A, B, C, D, 64, 64, 128, 0, None, 0, A + 64 * 96, None) == DEV   # after a_q
+    assert g6(A, B, C, D, 64, 64, 128, 0, None, 0, A + 64 * 80, None) == ALIAS
     q4 = L.tfq_quantize_mxfp4
     assert q4(A, 4, 128, 128, B, C, None) == DEV
     assert q4(A, 4, 96, 96, B, C, None) == SHAPE           # cols % 128
