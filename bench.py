@@ -105,6 +105,75 @@ def time_calls(torch, stream, fn, reps=20, warmup=5):
     return t[len(t) // 2], t[0]
 
 
+INFINITY_CACHE_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
+
+
+def cache_note(nbytes):
+    """Whether a kernel's input alone fits the Infinity Cache (a repeated
+    call then reads it from there: a "hot" figure)."""
+    fits = nbytes <= INFINITY_CACHE_BYTES
+    return f"{'hot' if fits else 'cold'} (input {nbytes / 2**20:.0f} MiB, Infinity Cache 256 MiB)"
+
+
+def time_cold(torch, stream, x, call, reps=20, warmup=5):
+    """Median / min of call(x_i) over rotating copies x_i of x whose total
+    size is at least twice the Infinity Cache, so each call reads its input
+    from HBM (a "cold" figure)."""
+    n = max(2, -(-2 * INFINITY_CACHE_BYTES // (x.numel() * x.element_size())))
+    copies = [x.clone() for _ in range(n)]
+    i = [0]
+
+    def fn():
+        call(copies[i[0] % n])
+        i[0] += 1
+
+    out = time_calls(torch, stream, fn, reps, warmup)
+    del copies
+    torch.cuda.empty_cache()
+    return out, n
+
+
+def sample_sclk(torch, fn, seconds=3.0):
+    """Shader clock while fn runs back to back: amd-smi sampled from a second
+    thread, averaged over the XCDs, after a 0.5 s ramp.  None without amd-smi."""
+    import shutil
+    import subprocess
+    import threading
+
+    if shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def worker():
+        t_start = time.perf_counter()
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                d = json.loads(r.stdout)
+                d = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                clk = [v["clk"]["value"] for k, v in d["clock"].items() if k.startswith("gfx_")]
+                if clk and time.perf_counter() - t_start > 0.5:
+                    samples.append(float(np.mean(clk)))
+            except Exception:  # noqa: BLE001 -- an unreadable sample is skipped
+                time.sleep(0.1)
+
+    th = threading.Thread(target=worker, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    return {"median_mhz": round(float(np.median(samples)), 1), "min_mhz": round(min(samples), 1),
+            "max_mhz": round(max(samples), 1), "samples": len(samples),
+            "during": "the up GEMM + GELU run back to back for 3 s (amd-smi, mean over 8 XCDs)"}
+
+
 def extras(torch, tfq, synth, stream):
     """Secondary workloads, each timed on its own (median of 20 after 5 warmup)."""
     out = {}
@@ -126,7 +195,13 @@ def extras(torch, tfq, synth, stream):
     qa, sa = tfq.tfq_quantize_rows(x, "fp8", 448.0)
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 0, qa, sa))
     gbs = quant_bytes(M, K) / med / 1e6
-    out["c3_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    out["c3_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                            "cache": cache_note(M * K * 2)}
+    (med, _), n = time_cold(torch, stream, x, lambda t: tfq.tfq_quantize_rows(t, "fp8", 448.0, 0,
+                                                                              qa, sa))
+    gbs = quant_bytes(M, K) / med / 1e6
+    out["c3_quantize_x_cold"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                 "cache": f"cold ({n} rotating input copies)"}
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 0, None,
                                                                       None, y))
     out["c3_gemm"] = {"ms": med, "tflops": fl / med / 1e9,
@@ -144,7 +219,13 @@ def extras(torch, tfq, synth, stream):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 128, qa, sa))
     gbs = quant_bytes(M, K, 128) / med / 1e6
-    out["c5_quantize_x_groups"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    out["c5_quantize_x_groups"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                   "cache": cache_note(M * K * 2)}
+    (med, _), n = time_cold(torch, stream, x, lambda t: tfq.tfq_quantize_rows(t, "fp8", 448.0, 128,
+                                                                              qa, sa))
+    gbs = quant_bytes(M, K, 128) / med / 1e6
+    out["c5_quantize_x_groups_cold"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                        "cache": f"cold ({n} rotating input copies)"}
     fl = 2.0 * M * N * K
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 128, None,
                                                                       None, y))
@@ -163,7 +244,13 @@ def extras(torch, tfq, synth, stream):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "int8", 127.0, 0, qa, sa))
     gbs = quant_bytes(M, K) / med / 1e6
-    out["c2_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    out["c2_quantize_x"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                            "cache": cache_note(M * K * 2)}
+    (med, _), n = time_cold(torch, stream, x, lambda t: tfq.tfq_quantize_rows(t, "int8", 127.0, 0,
+                                                                              qa, sa))
+    gbs = quant_bytes(M, K) / med / 1e6
+    out["c2_quantize_x_cold"] = {"ms": med, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                 "cache": f"cold ({n} rotating input copies)"}
     fl = 2.0 * M * N * K
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_int8(qa, sa, wq, ws, None, None,
                                                                        True, False, y))
@@ -410,8 +497,9 @@ def main():
         "gemm_down": {"ms": per["gemm_down"],
                       "tflops": 2.0 * M * N2 * N / (per["gemm_down"] * 1e-3) / 1e12},
     }
-    for kk in ("quant_x", "quant_g"):
+    for kk, nb in (("quant_x", M * K * 2), ("quant_g", M * N * 2)):
         kernels[kk]["frac_hbm"] = kernels[kk]["gbs"] / HBM_PEAK_GBS
+        kernels[kk]["cache"] = cache_note(nb)
     for kk, (n_, k_, epi_) in (("gemm_up_gelu", (N, K, "gelu_tanh")), ("gemm_down", (N2, N, None))):
         cfg = tfq.tfq_autotune_lookup("fp8", M, n_, k_, epi_)
         kernels[kk]["config"] = None if cfg is None else {"kernel": cfg[0], "band": cfg[1]}
@@ -428,6 +516,13 @@ def main():
         torch.cuda.synchronize()
         sweep[str(q)] = {"ms_per_step": (time.perf_counter() - t1) * 1e3 / 3}
     timer.clear()
+    log("shader clock under the up GEMM (amd-smi)")
+    sclk = sample_sclk(torch, lambda: tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None,
+                                                            "gelu_tanh", g))
+    if sclk is not None:
+        sclk["frac_fp8_peak_at_this_clock"] = round(
+            achieved / (FP8_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 4)
+    roofline["sclk"] = sclk
 
     ext = {}
     if not args.no_extras:
