@@ -395,11 +395,14 @@ void gemm_pipe_kernel(const Params p)
     // the fragment reads that go with MFMA i of a K step: one 16-byte half
     // each (16 per K step), or for MXFP6 one or two 8-byte pieces (24)
     auto read_slots = [&](int buf, int ks, Frags& f, int i) {
+        // fragment order A0, B0..B3, A1..A3: the order the next K step's
+        // MFMAs first use them
+        constexpr int ord[8] = {4, 0, 1, 2, 3, 5, 6, 7};
         if constexpr (FP6) {
 #pragma unroll
-            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, sl / 3, sl % 3);
+            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, ord[sl / 3], sl % 3);
         } else {
-            read_part(buf, ks, f, i >> 1, i & 1);
+            read_part(buf, ks, f, ord[i >> 1], i & 1);
         }
     };
     // weights as the first operand: the 32x32 result is the transposed
