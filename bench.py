@@ -14,7 +14,7 @@ on the stream it runs on), the oracle timed on host cores on a row sample,
 and per-workload extras (image-DiT FFN-up fused Linear, block-scaled FP8,
 INT8, quantiser GB/s).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu] [--no-clock]
 """
 from __future__ import annotations
 
@@ -406,6 +406,8 @@ def main():
                     help="use the fixed heuristic GEMM configurations instead of tuning each "
                          "shape on its first call (during warm-up)")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 3 s shader-clock sample (amd-smi) after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -516,9 +518,11 @@ def main():
         torch.cuda.synchronize()
         sweep[str(q)] = {"ms_per_step": (time.perf_counter() - t1) * 1e3 / 3}
     timer.clear()
-    log("shader clock under the up GEMM (amd-smi)")
-    sclk = sample_sclk(torch, lambda: tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None,
-                                                            "gelu_tanh", g))
+    sclk = None
+    if not args.no_clock:
+        log("shader clock under the up GEMM (amd-smi)")
+        sclk = sample_sclk(torch, lambda: tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None,
+                                                                "gelu_tanh", g))
     if sclk is not None:
         sclk["frac_fp8_peak_at_this_clock"] = round(
             achieved / (FP8_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 4)
