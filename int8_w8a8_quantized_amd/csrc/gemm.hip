@@ -750,16 +750,19 @@ void gemm_pipe_kernel(const Params p)
 // ---------------------------------------------------------------------------
 // Block-scaled FP8 kernel: 1x128 activation groups and 128x128 weight blocks
 // (LightX2V "模型量化技术", table "量化模式", fp8-b128-deepgemm).  256x128
-// output tile, 4 waves (2x2) of 128x64, so every wave's 64 columns lie in one
-// 128-wide weight block and -- with the weights as the first MFMA operand --
-// every lane's output row is fixed per 32-row tile: the scale of a
-// (row, K-block) pair is one float per row tile.  One stage is one 128-deep
-// K block (two K steps of MFMAs into a temporary); the next block's first K
-// step folds it in, acc += temp * (s_a[row, kb] * s_b[nb, kb]), one tile
-// before each of its MFMAs.  Operands go straight into LDS (LDS-DMA loads,
-// whole 128-byte lines), 3 LDS buffers, loads 3 stages ahead, one barrier
-// per stage; the row scales of each block come with the stage (4-byte
-// LDS-DMA loads), the weight block's scale by a scalar load.
+// output tile, 8 waves (4x2) of 64x64, two per SIMD: every wave's 64 columns
+// lie in one 128-wide weight block and -- with the weights as the first MFMA
+// operand -- every lane's output row is fixed per 32-row tile, so the scale
+// of a (row, K-block) pair is one float per row tile.  One stage is one
+// 128-deep K block (two K steps of MFMAs into a temporary); the next block's
+// first K step folds it in, acc += temp * (s_a[row, kb] * s_b[nb, kb]), just
+// before each tile's first MFMA.  A wave's sums and temporaries (2 x 64
+// registers) both stay in VGPRs, so the fold is one FMA per element, and the
+// two waves of a SIMD hide each other's fold, barrier and memory waits.
+// Operands go straight into LDS (LDS-DMA loads, whole 128-byte lines), 3
+// LDS buffers, loads 3 stages ahead, one barrier per stage; the row scales
+// of each block come with the stage (4-byte LDS-DMA loads), the weight
+// block's scales once per tile.
 // ---------------------------------------------------------------------------
 constexpr int QK = 64;                     // K bytes per stage
 constexpr int QA = BM * QK;                // 16 KB of A per stage
@@ -777,13 +780,13 @@ constexpr int XB_SMEM = XB_SB + 4096;
 
 
 template <int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void gemm_block_kernel(const Params p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[XB_SMEM];
 
     const int wave_u = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int wm = wave_u & 1, wn = wave_u >> 1;
+    const int wm = wave_u & 3, wn = wave_u >> 2;  // rows wm*64 .. +63, columns wn*64 .. +63
     const int lane = lane_id_here();
     int tm, tn;
     map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -796,31 +799,35 @@ void gemm_block_kernel(const Params p)
     const v4i rsa = buffer_rsrc(p.sa + (int64_t)m0 * KT, rows_a * KT * 4);
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-    // global -> LDS: wave w moves 8-row groups 8 w + j (j < 8) of A and
-    // 4 w + j (j < 4) of B per stage, one 1 KB LDS-DMA load each; lane l
+    // global -> LDS: wave w moves 8-row groups 4 w + j (j < 4) of A and
+    // 2 w + j (j < 2) of B per stage, one 1 KB LDS-DMA load each; lane l
     // lands at row l >> 3, physical chunk l & 7 of its group and fetches
     // logical chunk (l & 7) ^ ((row >> 1) & 7) (the LDS swizzle for 128-byte
     // rows), which is (l & 7) ^ (l >> 4) in even groups and that ^ 4 in odd.
     const int lc_e = (lane & 7) ^ (lane >> 4), lc_o = lc_e ^ 4;
-    const int a_off = (64 * wave_u + (lane >> 3)) * K;
-    const int b_off = (32 * wave_u + (lane >> 3)) * K;
-    // the row scales of block kb: wave w fetches rows 64 w + lane
-    const int sa_off = (64 * wave_u + lane) * KT * 4;
-    auto dma_stage = [&](int kt, int buf) {
+    const int a_off = (32 * wave_u + (lane >> 3)) * K;
+    const int b_off = (16 * wave_u + (lane >> 3)) * K;
+    // the row scales of block kb: waves w and w + 4 both fetch rows
+    // 64 (w & 3) + lane (the same bytes to the same LDS place), so every wave
+    // issues the same number of loads per stage
+    const int sa_off = (64 * (wave_u & 3) + lane) * KT * 4;
+    // load d (0..6) of stage kt into LDS buffer bf: 4 of A, 2 of B, row scales
+    auto dma_op = [&](int kt, int bf, int d) {
         const int k0 = kt * 128;
-        const int oob_e = (int)((unsigned)(k0 + lc_e * 16 >= K) << 31);
-        const int oob_o = (int)((unsigned)(k0 + lc_o * 16 >= K) << 31);
-        const uint32_t dst = lds_base + (uint32_t)(buf * XB_STAGE);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int lc = (j & 1) ? lc_o : lc_e, oob = (j & 1) ? oob_o : oob_e;
-            lds_dma16(ra, (a_off + j * 8 * K + k0 + lc * 16) | oob, dst + (8 * wave_u + j) * 1024);
-            if (j < 4)
+        const uint32_t dst = lds_base + (uint32_t)(bf * XB_STAGE);
+        if (d < 6) {
+            const int j = d < 4 ? d : d - 4;
+            const int lc = (j & 1) ? lc_o : lc_e;
+            const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
+            if (d < 4)
+                lds_dma16(ra, (a_off + j * 8 * K + k0 + lc * 16) | oob, dst + (4 * wave_u + j) * 1024);
+            else
                 lds_dma16(rb, (b_off + j * 8 * K + k0 + lc * 16) | oob,
-                          dst + XB_A + (4 * wave_u + j) * 1024);
+                          dst + XB_A + (2 * wave_u + j) * 1024);
+        } else {
+            lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
+                     lds_base + XB_SA + bf * 1024 + (wave_u & 3) * 256);
         }
-        lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
-                 lds_base + XB_SA + buf * 1024 + wave_u * 256);
     };
 
     // LDS -> fragments: K step ks (0, 1) of a stage, lane reads row
@@ -831,66 +838,51 @@ void gemm_block_kernel(const Params p)
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 2; ++e) rd[ks][e] = fr * 128 + (((4 * ks + 2 * h + e) ^ sw) << 4);
-    const int a_rd = wm * 128 * 128;
+    const int a_rd = wm * 64 * 128;
     const int b_rd = XB_A + wn * 64 * 128;
     struct Frags {
-        v8i b[2], a[4];
+        v8i b[2], a[2];
     };
-    // half e of fragment q (B tiles 0, 1, then A tiles 0..3) of K step ks
-    auto read_part = [&](int buf, int ks, Frags& f, int q, int e) {
+    // fragment q (B tiles 0, 1, then A tiles 0, 1) of K step ks, both halves
+    auto read_frag = [&](int buf, int ks, Frags& f, int q) {
         const uint8_t* s = smem + buf * XB_STAGE + (q < 2 ? b_rd + q * 32 * 128 : a_rd + (q - 2) * 32 * 128);
-        const v4i v = *reinterpret_cast<const v4i*>(s + rd[ks][e]);
         v8i& d = q < 2 ? f.b[q] : f.a[q - 2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
-    };
-
-    v16f acc[4][2], tmp[4][2];
+        for (int e = 0; e < 2; ++e) {
+            const v4i v = *reinterpret_cast<const v4i*>(s + rd[ks][e]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
+        }
+    };
+    // fragments in the order the K step's MFMAs first use them: A0, B0, B1, A1
+    constexpr int ord[4] = {2, 0, 1, 3};
+
+    v16f acc[2][2], tmp[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    float f_prev[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // block scale factors of the previous stage
+    float f_prev[2] = {0.0f, 0.0f};  // block scale factors of the previous stage
 
     // prologue: bias and the weight block's scales of every K block (wave
-    // 3; the tile's 128 columns are one weight block), stages 0, 1, 2
-    if (wave_u == 3) {
+    // 7; the tile's 128 columns are one weight block), stages 0, 1, 2
+    if (wave_u == 7) {
         if (p.bias != nullptr) lds_dma4(buffer_rsrc(p.bias + n0, rows_b * 2), lane * 4, lds_base + XB_BIAS);
         const v4i rsb = buffer_rsrc(p.sb + (int64_t)(n0 >> 7) * KT, KT * 4);
         for (int c = 0; c < KT; c += 64) lds_dma4(rsb, (c + lane) * 4, lds_base + XB_SB + c * 4);
     }
-    dma_stage(0, 0);
-    dma_stage(1, 1);
-    dma_stage(2, 2);
-    // bias and stage 0 complete: 26 loads (stages 1, 2) may be in flight
-    asm volatile("s_waitcnt vmcnt(26)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int st = 0; st < 3; ++st)
+#pragma unroll
+        for (int d = 0; d < 7; ++d) dma_op(st, st, d);
+    // bias, block scales and stage 0 complete: 14 loads (stages 1, 2) may be in flight
+    asm volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
     Frags f0, f1;
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
-        read_part(0, 0, f0, q, 0);
-        read_part(0, 0, f0, q, 1);
-    }
+    for (int q = 0; q < 4; ++q) read_frag(0, 0, f0, ord[q]);
 
-    // DMA op d (0..12) of stage kt into buffer bf: A groups, B groups, row scales
-    auto dma_op = [&](int kt, int bf, int d) {
-        const int k0 = kt * 128;
-        const uint32_t dst = lds_base + (uint32_t)(bf * XB_STAGE);
-        if (d < 12) {
-            const int j = d < 8 ? d : d - 8;
-            const int lc = (j & 1) ? lc_o : lc_e;
-            const int oob = (int)((unsigned)(k0 + lc * 16 >= K) << 31);
-            if (d < 8)
-                lds_dma16(ra, (a_off + j * 8 * K + k0 + lc * 16) | oob, dst + (8 * wave_u + j) * 1024);
-            else
-                lds_dma16(rb, (b_off + j * 8 * K + k0 + lc * 16) | oob,
-                          dst + XB_A + (4 * wave_u + j) * 1024);
-        } else {
-            lds_dma4(rsa, (sa_off + kt * 4) | (int)((unsigned)(kt >= KT) << 31),
-                     lds_base + XB_SA + bf * 1024 + wave_u * 256);
-        }
-    };
     auto mfma = [&](const v16f& c, const Frags& f, int mi, int ni) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], c, 0, 0, 0, 0, 0, 0);
     };
@@ -899,7 +891,7 @@ void gemm_block_kernel(const Params p)
     // Stage kt lives in LDS buffer kt % 3.  Its barrier sits between its two
     // K steps: by then every wave has read all of its fragments and row
     // scales and has received its own loads of stage kt + 1 (loads issued
-    // after those: the 13 of stage kt + 2), so the buffer is free for stage
+    // after those: the 7 of stage kt + 2), so the buffer is free for stage
     // kt + 3, whose loads go out during the second K step together with the
     // reads of stage kt + 1's first fragments.
     int buf = 0;
@@ -907,14 +899,14 @@ void gemm_block_kernel(const Params p)
         const int nbuf = buf == XB_BUF - 1 ? 0 : buf + 1;
         const float sbv = reinterpret_cast<const float*>(smem + XB_SB)[kt];
         const float* sa_l = reinterpret_cast<const float*>(smem + XB_SA + buf * 1024);
-        float f_cur[4];
+        float f_cur[2];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) f_cur[mi] = sa_l[wm * 128 + mi * 32 + fr];
+        for (int mi = 0; mi < 2; ++mi) f_cur[mi] = sa_l[wm * 64 + mi * 32 + fr];
         // K step 0: fold the previous block's temporary of each tile into acc
-        // just before the tile's first MFMA of this block; K step 1's 12
-        // fragment halves into f1 (1 or 2 after each MFMA)
+        // just before the tile's first MFMA of this block; K step 1's
+        // fragments into f1, one after each MFMA
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int mi = i >> 1, ni = i & 1;
             if (kt > 0) {
 #pragma unroll
@@ -923,44 +915,42 @@ void gemm_block_kernel(const Params p)
             }
             tmp[mi][ni] = mfma(v16f{}, f0, mi, ni);
             TFQ_FENCE();
-#pragma unroll
-            for (int r = (12 * i) / 8; r < (12 * (i + 1)) / 8; ++r) read_part(buf, 1, f1, r >> 1, r & 1);
+            read_frag(buf, 1, f1, ord[i]);
             TFQ_FENCE();
         }
-        asm volatile("s_waitcnt vmcnt(13)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(7)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // K step 1; stage kt+1's K step 0 fragments into f0; stage kt+3's loads
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int mi = i >> 1, ni = i & 1;
             tmp[mi][ni] = mfma(tmp[mi][ni], f1, mi, ni);
             TFQ_FENCE();
+            read_frag(nbuf, 0, f0, ord[i]);
 #pragma unroll
-            for (int r = (12 * i) / 8; r < (12 * (i + 1)) / 8; ++r) read_part(nbuf, 0, f0, r >> 1, r & 1);
-#pragma unroll
-            for (int d = (13 * i) / 8; d < (13 * (i + 1)) / 8; ++d) dma_op(kt + 3, buf, d);
+            for (int d = (7 * i) / 4; d < (7 * (i + 1)) / 4; ++d) dma_op(kt + 3, buf, d);
             TFQ_FENCE();
         }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) f_prev[mi] = f_cur[mi] * sbv;
+        for (int mi = 0; mi < 2; ++mi) f_prev[mi] = f_cur[mi] * sbv;
         buf = nbuf;
     }
 #undef TFQ_FENCE
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[mi][ni][e] = __builtin_fmaf(tmp[mi][ni][e], f_prev[mi], acc[mi][ni][e]);
 
-    // ---- epilogue: lane holds row wm*128 + mi*32 + fr and columns
+    // ---- epilogue: lane holds row wm*64 + mi*32 + fr and columns
     // wn*64 + ni*32 + 8q + 4h + (0..3) in registers 4q..4q+3.  Bias is always
     // added (-0.0 without one leaves every value unchanged). ----
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past the last block
     lds_barrier();
     const bool has_bias = p.bias != nullptr;
     const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + XB_BIAS);
-    uint8_t* stg = smem + wave_u * 128 * QEPITCH;
+    uint8_t* stg = smem + wave_u * 64 * QEPITCH;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
@@ -972,7 +962,7 @@ void gemm_block_kernel(const Params p)
                                  has_bias ? __uint_as_float(b2.y << 16) : -0.0f,
                                  has_bias ? __uint_as_float(b2.y & 0xffff0000u) : -0.0f};
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+            for (int mi = 0; mi < 2; ++mi) {
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -984,22 +974,22 @@ void gemm_block_kernel(const Params p)
             }
         }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // a wave reads back only its own rows
     const int ch = lane & 7;
     const int gcol = n0 + wn * 64 + ch * 8;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 8; ++j) {
         const int lrow = j * 8 + (lane >> 3);
         const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * QEPITCH + ch * 16);
-        const int grow = m0 + wm * 128 + lrow;
+        const int grow = m0 + wm * 64 + lrow;
         if (grow < p.m && gcol < p.n)
             *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Two-workgroups-per-CU kernel for per-token / per-channel scales: the
-// block kernel's 256x128 tile and 4 waves of 128x64, with at most 256
+// Two-workgroups-per-CU kernel for per-token / per-channel scales: a
+// 256x128 tile and 4 waves of 128x64, with at most 256
 // registers per wave and 72 KB of LDS per workgroup so that two workgroups
 // share every CU; each SIMD then interleaves the MFMAs of two independent
 // waves, which hides one workgroup's barrier and memory waits behind the
@@ -1201,7 +1191,7 @@ hipError_t launch_block(Params p, hipStream_t st)
 {
     p.tiles_n = (p.n + QBN - 1) / QBN;
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    hipLaunchKernelGGL((gemm_block_kernel<EPI>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_block_kernel<EPI>), dim3(grid), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
