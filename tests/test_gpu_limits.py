@@ -1,6 +1,7 @@
 """GEMMs at the largest K each entry point accepts, so that every 32-bit
 buffer offset and record count runs at its bound: FP8 on both kernels
-(K = 2^22), MXFP8 (K = 2^22) and MXFP4 (K = 2^23).  Codes are random on the
+(K = 2^22), MXFP8 (K = 2^22), MXFP4 (K = 2^23) and block-scaled FP8
+(K = 2^17).  Codes are random on the
 device; outputs are checked on sampled rows x columns against the oracle
 (which takes the matching rows of the operands).  MX scales change with the
 K block (a different power of two every block), so a misplaced scale word
@@ -11,7 +12,8 @@ import pytest
 import torch
 
 import oracle as orc
-from gpu_util import assert_fp8_tolerance, host_bits, mx_grouped, needs_gpu, say
+import synth
+from gpu_util import assert_fp8_tolerance, dev_bf16, host_bits, mx_grouped, needs_gpu, say
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -76,3 +78,45 @@ def test_mx_max_k(tfq, fp4):
     ref = ref_fn(host_bits(a[r]), np.repeat(row[None, :], ROWS.size, 0), host_bits(b[c]),
                  np.repeat(row[None, :], cols.size, 0))
     assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, f"mx max K fp4={fp4}")
+
+
+def test_block_scaled_max_k(tfq):
+    """Block-scaled FP8 at the largest K (131072: the weight blocks' scale
+    row fills its 4 KB of LDS), ragged M, bias and GELU, with row scales and
+    weight-block scales that change with every K block."""
+    M, N, K = 300, 256, 1 << 17
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a, b = _codes(g, M, K), _codes(g, N, K)
+    kb = torch.arange(K // 128, device="cuda", dtype=torch.float32)
+    sa = (torch.rand((M, K // 128), device="cuda", generator=g) + 0.5) * torch.exp2(kb % 7 - 3) * 1e-3
+    sb = (torch.rand((N // 128, K // 128), device="cuda", generator=g) + 0.5) * 1e-3
+    rng = np.random.default_rng(7)
+    bias = synth.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    say(f"block-scaled max K: M={M} N={N} K={K}")
+    y = tfq.tfq_scaled_mm_fp8(a, sa, b, sb, 128, dev_bf16(bias), "gelu_tanh")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 150, 255, 256, 299])
+    ref = orc.linear_ref(host_bits(a), host_bits(sa), host_bits(b), host_bits(sb), "fp8", 128,
+                         bias=bias, gelu=True, rows=rows)
+    assert_fp8_tolerance(host_bits(y)[rows], ref, "block-scaled max K")
+
+
+def test_mx6_max_k(tfq):
+    """MXFP6 (E3M2) at the largest K (2^22: 3 MiB code rows)."""
+    M, N, K = 512, 264, 1 << 22
+    kb = K // 4 * 3
+    g = torch.Generator(device="cuda").manual_seed(4)
+    a = torch.randint(0, 256, (M, kb), dtype=torch.uint8, device="cuda", generator=g)
+    b = torch.randint(0, 256, (N, kb), dtype=torch.uint8, device="cuda", generator=g)
+    row = _mx_scale_row(K)
+    grouped_row = torch.from_numpy(mx_grouped(row[None, :])).cuda()
+    sa = grouped_row.expand(K // 128, M, 4).contiguous()
+    sb = grouped_row.expand(K // 128, N, 4).contiguous()
+    say(f"mx6 max K: M={M} N={N} K={K}")
+    y = tfq.tfq_scaled_mm_mxfp6(a, sa, b, sb, "e3m2")
+    torch.cuda.synchronize()
+    cols = np.array([0, 7, 200, N - 1])
+    r, c = torch.from_numpy(ROWS), torch.from_numpy(cols)
+    ref = orc.linear_mx6_ref(host_bits(a[r]), np.repeat(row[None, :], ROWS.size, 0), host_bits(b[c]),
+                             np.repeat(row[None, :], cols.size, 0), "e3m2")
+    assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, "mx6 max K")
