@@ -122,6 +122,20 @@ __device__ __forceinline__ uint2 encode_chunk(const uint4& v, const Quotient& d,
     return o;
 }
 
+// Streaming reads of the per-row quantisers and the KV-cache store: every
+// input element is read once, so the loads are marked non-temporal and the
+// caches (L2, Infinity Cache) may drop those lines first.  Quantising X and
+// G of the video-DiT FFN pair ran 12% and 7% faster so; the MX and 1x128
+// group kernels ran 2-4% slower and keep plain loads.  The codes are stored
+// normally: the GEMM that follows reads them, and non-temporal stores made
+// it ~3% slower.  Values are unaffected.
+typedef uint32_t nt_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p)
+{
+    const nt_u4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
 
 // Source of output row `row`: the row itself, or row gather[row] of x for a
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(256) void quantize_rows_resident(
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = c * 64 + lane;
-        v[c] = (idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        v[c] = (idx < nchunk) ? load_stream(xr + idx) : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t m = 0;
 #pragma unroll
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(256) void quantize_rows_split(
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = (part * CH + c) * 64 + lane;
-        v[c] = (ok && idx < nchunk) ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        v[c] = (ok && idx < nchunk) ? load_stream(xr + idx) : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t m = 0;
 #pragma unroll
@@ -463,7 +477,7 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
         tok[u] = in[u] ? v / heads : 0;
         h[u] = in[u] ? v - tok[u] * heads : 0;
         x[u] = (in[u] && lane_on)
-                   ? reinterpret_cast<const uint4*>(kv + (int64_t)tok[u] * ld_token + (int64_t)h[u] * hd)[li]
+                   ? load_stream(reinterpret_cast<const uint4*>(kv + (int64_t)tok[u] * ld_token + (int64_t)h[u] * hd) + li)
                    : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
