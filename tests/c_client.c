@@ -1,0 +1,70 @@
+/* A plain C11 client of include/tfq.h: compiled and run by
+ * tests/test_c_client.py (no GPU needed).  Checks that the header is valid
+ * C, that every declared entry point links against libtfq.so, and that host
+ * validation answers through the C ABI: bad arguments come back as status
+ * codes before any HIP call, with a message for each. */
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "tfq.h"
+
+static int fails = 0;
+#define EXPECT(cond)                                                    \
+    do {                                                                \
+        if (!(cond)) {                                                  \
+            printf("FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);      \
+            ++fails;                                                    \
+        }                                                               \
+    } while (0)
+
+/* every entry point, taken by address so that a missing symbol fails the link */
+typedef void (*fn_t)(void);
+static const fn_t entry_points[] = {
+    (fn_t)tfq_quantize_rows,           (fn_t)tfq_quantize_rows_gather,
+    (fn_t)tfq_quantize_weight_per_channel, (fn_t)tfq_scaled_mm_fp8,
+    (fn_t)tfq_scaled_mm_int8,          (fn_t)tfq_grouped_scaled_mm_fp8,
+    (fn_t)tfq_quant_linear_workspace_bytes, (fn_t)tfq_quant_linear_fused,
+    (fn_t)tfq_quantize_mx,             (fn_t)tfq_scaled_mm_mxfp8,
+    (fn_t)tfq_quantize_mxfp4,          (fn_t)tfq_scaled_mm_mxfp4,
+    (fn_t)tfq_quantize_mxfp6,          (fn_t)tfq_scaled_mm_mxfp6,
+    (fn_t)tfq_kv_cache_store,          (fn_t)tfq_kv_cache_load,
+    (fn_t)tfq_set_autotune,            (fn_t)tfq_autotune_lookup,
+    (fn_t)tfq_autotune_clear,          (fn_t)tfq_e4m3fn_encode_f32,
+    (fn_t)tfq_status_string,           (fn_t)tfq_last_hip_error,
+    (fn_t)tfq_abi_version,
+};
+
+int main(void)
+{
+    for (size_t i = 0; i < sizeof entry_points / sizeof entry_points[0]; ++i)
+        EXPECT(entry_points[i] != NULL);
+    EXPECT(tfq_abi_version() == TFQ_ABI_VERSION);
+
+    /* every status has a message */
+    for (int s = TFQ_OK; s <= TFQ_ERR_HIP; ++s) {
+        const char* msg = tfq_status_string((tfq_status)s);
+        EXPECT(msg != NULL && strlen(msg) > 0);
+    }
+
+    /* host validation, before any HIP call (addresses never dereferenced) */
+    static uint8_t host[1 << 16];
+    uint8_t* p = (uint8_t*)(((uintptr_t)host + 255) & ~(uintptr_t)255);
+    EXPECT(tfq_quantize_rows(NULL, 4, 128, 128, TFQ_QTYPE_E4M3FN, 448.0f, 0, p, (float*)(p + 4096), NULL) ==
+           TFQ_ERR_NULL_POINTER);
+    EXPECT(tfq_quantize_rows(p, 4, 100, 128, TFQ_QTYPE_E4M3FN, 448.0f, 0, p + 4096, (float*)(p + 8192), NULL) ==
+           TFQ_ERR_BAD_SHAPE);                                        /* cols % 16 */
+    EXPECT(tfq_quantize_rows(p, 4, 128, 128, TFQ_QTYPE_E4M3FN, 21.0f, 0, p + 4096, (float*)(p + 8192), NULL) ==
+           TFQ_ERR_BAD_QMAX);                                         /* not on the E4M3FN grid */
+    EXPECT(tfq_scaled_mm_int8((const int8_t*)p, (const float*)(p + 4096), (const int8_t*)(p + 8192),
+                              (const float*)(p + 12288), 16, 16, 131072, NULL, TFQ_EPI_NONE,
+                              p + 16384, NULL, NULL) == TFQ_ERR_BAD_SHAPE); /* INT32 overflow bound */
+    EXPECT(tfq_scaled_mm_fp8(p, (const float*)(p + 4096), p + 8192, (const float*)(p + 12288), 16, 16, 128,
+                             0, NULL, TFQ_EPI_GELU_TANH, p, NULL) == TFQ_ERR_ALIAS); /* y over a_q */
+    EXPECT(tfq_quant_linear_workspace_bytes(1024, 4096, TFQ_QTYPE_E4M3FN, 0) >= (size_t)1024 * 4096);
+    EXPECT(tfq_set_autotune(2) == TFQ_ERR_UNSUPPORTED);
+
+    if (fails == 0) printf("c client ok: %zu entry points, ABI %d\n",
+                           sizeof entry_points / sizeof entry_points[0], tfq_abi_version());
+    return fails != 0;
+}
