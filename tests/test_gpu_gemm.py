@@ -176,6 +176,46 @@ def test_fused_linear_matches_two_calls_and_oracle(tfq, qtype, qmax):
         assert np.array_equal(host_bits(y), y_e)
 
 
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+def test_fused_linear_strided_input_gelu(tfq, qtype):
+    """The fused call on a column slice of a wider tensor (row stride ld_x >
+    k) with the GELU epilogue equals quantising the same slice and the GEMM
+    with GELU; QuantLinear in block mode equals the fused block call."""
+    M, N, K, LD = 300, 264, 512, 640
+    rng = np.random.default_rng(29)
+    x = (rng.standard_normal((M, LD)) * np.exp2(rng.integers(-3, 4, (M, 1)))).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bias = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    xb, wb, bb = synth.to_bf16_bits(x), synth.to_bf16_bits(w), synth.to_bf16_bits(bias)
+    qmax = 448.0 if qtype == "fp8" else 127.0
+    say(f"quant_linear_fused strided {qtype} M={M} N={N} K={K} ld={LD}")
+    xd = dev_bf16(xb)[:, :K]
+    assert xd.stride(0) == LD
+    wq, ws = tfq.tfq_quantize_weight_per_channel(dev_bf16(wb), qtype, qmax)
+    y = tfq.tfq_quant_linear_fused(xd, wq, ws, qtype, qmax, 0, dev_bf16(bb), "gelu_tanh")
+    qa, sa = tfq.tfq_quantize_rows(xd, qtype, qmax)
+    if qtype == "fp8":
+        y2 = tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 0, dev_bf16(bb), "gelu_tanh")
+    else:
+        y2, _ = tfq.tfq_scaled_mm_int8(qa, sa, wq, ws, dev_bf16(bb), "gelu_tanh")
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y), host_bits(y2))
+    qa_e, sa_e = orc.quantize_rows(np.ascontiguousarray(xb[:, :K]), qtype, qmax)
+    qb_e, sb_e = orc.quantize_rows(wb, qtype, qmax)
+    assert np.array_equal(host_bits(qa).view(np.uint8), qa_e.view(np.uint8))
+    ref = orc.linear_ref(qa_e, sa_e, qb_e, sb_e, qtype, bias=bb, gelu=True)
+    assert_fp8_tolerance(host_bits(y), ref, f"fused strided {qtype}")
+    if qtype == "fp8":
+        # block mode needs N % 128 == 0: the first 256 weight rows
+        wd2, bd2 = dev_bf16(np.ascontiguousarray(wb[:256])), dev_bf16(bb[:256])
+        lin = tfq.QuantLinear(wd2, bd2, scale_block=128, epi="gelu_tanh")
+        yl = lin(xd)
+        wqb, wsb = tfq.tfq_quantize_weight_per_channel(wd2, "fp8", 448.0, 128)
+        yb = tfq.tfq_quant_linear_fused(xd, wqb, wsb, "fp8", 448.0, 128, bd2, "gelu_tanh")
+        torch.cuda.synchronize()
+        assert torch.equal(yl, yb)
+
+
 def test_quant_linear_module_caches_weight(tfq):
     M, N, K = 100, 256, 256
     xb, wb, _, _, _, _, _ = _operands(3, M, N, K, "fp8")
