@@ -169,3 +169,26 @@ def test_quant_linear_mx_modes(tfq, qtype):
     torch.cuda.synchronize()
     assert lin.w_q is wq
     assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+def test_mxfp4_tuned_config_same_bits(tfq):
+    """The tuned launch configuration of an MXFP4 GEMM gives the default
+    configuration's bits and is recorded under the MXFP4 kind."""
+    M, N, K = 700, 1024, 1024
+    _, _, qa, sa, qb, sb, bias = _operands(31, M, N, K)
+    a, b = dev_u8(qa), dev_u8(qb)
+    sad, sbd = dev_u8(mx_grouped(sa)), dev_u8(mx_grouped(sb))
+    say(f"autotune mxfp4 M={M} N={N} K={K}")
+    y0 = tfq.tfq_scaled_mm_mxfp4(a, sad, b, sbd, dev_bf16(bias), "gelu_tanh")
+    tfq.tfq_autotune_clear()
+    try:
+        tfq.tfq_set_autotune(1)
+        y1 = tfq.tfq_scaled_mm_mxfp4(a, sad, b, sbd, dev_bf16(bias), "gelu_tanh")
+        y2 = tfq.tfq_scaled_mm_mxfp4(a, sad, b, sbd, dev_bf16(bias), "gelu_tanh")
+        torch.cuda.synchronize()
+        cfg = tfq.tfq_autotune_lookup("mxfp4", M, N, K, "gelu_tanh")
+    finally:
+        tfq.tfq_set_autotune(0)
+        tfq.tfq_autotune_clear()
+    assert torch.equal(y0, y1) and torch.equal(y0, y2)
+    assert cfg is not None and cfg[0] == 0 and cfg[1] in (1, 2, 4, 8)
