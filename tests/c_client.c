@@ -48,7 +48,7 @@ int main(void)
     }
 
     /* host validation, before any HIP call (addresses never dereferenced) */
-    static uint8_t host[1 << 16];
+    static uint8_t host[1 << 17];
     uint8_t* p = (uint8_t*)(((uintptr_t)host + 255) & ~(uintptr_t)255);
     EXPECT(tfq_quantize_rows(NULL, 4, 128, 128, TFQ_QTYPE_E4M3FN, 448.0f, 0, p, (float*)(p + 4096), NULL) ==
            TFQ_ERR_NULL_POINTER);
@@ -63,6 +63,38 @@ int main(void)
                              0, NULL, TFQ_EPI_GELU_TANH, p, NULL) == TFQ_ERR_ALIAS); /* y over a_q */
     EXPECT(tfq_quant_linear_workspace_bytes(1024, 4096, TFQ_QTYPE_E4M3FN, 0) >= (size_t)1024 * 4096);
     EXPECT(tfq_set_autotune(2) == TFQ_ERR_UNSUPPORTED);
+
+    /* one error path of every other entry point */
+    const float* f = (const float*)(p + 4096);
+    EXPECT(tfq_quantize_rows_gather(p, 8, 128, 128, NULL, 4, TFQ_QTYPE_E4M3FN, 448.0f, 0, p + 4096,
+                                    (float*)(p + 8192), NULL) == TFQ_ERR_NULL_POINTER);
+    EXPECT(tfq_quantize_weight_per_channel(p, 100, 128, TFQ_QTYPE_E4M3FN, 448.0f, 128, p + 32768,
+                                           (float*)(p + 49152), NULL) == TFQ_ERR_BAD_SHAPE); /* n % 128 */
+    EXPECT(tfq_grouped_scaled_mm_fp8(p, f, p + 8192, f, (const int32_t*)(p + 12288), 0, 16, 16, 128,
+                                     NULL, TFQ_EPI_NONE, p + 16384, NULL) != TFQ_OK);  /* no groups */
+    EXPECT(tfq_quant_linear_fused(p, 16, 128, 128, p + 4096, f, 16, TFQ_QTYPE_E4M3FN, 448.0f, 0, NULL,
+                                  TFQ_EPI_NONE, p + 8192, p + 16384, 16, NULL) ==
+           TFQ_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(tfq_quantize_mx(p, 4, 100, 128, p + 4096, (uint32_t*)(p + 8192), NULL) == TFQ_ERR_BAD_SHAPE);
+    EXPECT(tfq_scaled_mm_mxfp8(p, (const uint32_t*)f, p + 8192, (const uint32_t*)f, 16, 16, 100, NULL,
+                               TFQ_EPI_NONE, p + 16384, NULL) == TFQ_ERR_BAD_SHAPE);
+    EXPECT(tfq_quantize_mxfp4(p + 2, 4, 128, 128, p + 4096, (uint32_t*)(p + 8192), NULL) ==
+           TFQ_ERR_MISALIGNED);
+    EXPECT(tfq_scaled_mm_mxfp4(p, (const uint32_t*)f, p + 8192, (const uint32_t*)f, 16, 16, 128, NULL,
+                               7, p + 16384, NULL) == TFQ_ERR_UNSUPPORTED);        /* epilogue */
+    EXPECT(tfq_quantize_mxfp6(p, 4, 128, 128, 5, p + 4096, (uint32_t*)(p + 8192), NULL) ==
+           TFQ_ERR_UNSUPPORTED);                                             /* format */
+    EXPECT(tfq_scaled_mm_mxfp6(p, (const uint32_t*)f, p + 8192, (const uint32_t*)f, 16, 16, 192, 0, NULL,
+                               TFQ_EPI_NONE, p + 16384, NULL) == TFQ_ERR_BAD_SHAPE); /* k % 128 */
+    EXPECT(tfq_kv_cache_store(p, 4, 2, 128, 256, NULL, 10, 448.0f, p + 4096, (float*)(p + 8192), NULL) ==
+           TFQ_ERR_NULL_POINTER);
+    EXPECT(tfq_kv_cache_load(p, f, 10, 2, 128, (const int32_t*)(p + 8192), 4, 9, p + 16384, NULL) ==
+           TFQ_ERR_UNSUPPORTED);                                             /* output dtype */
+    EXPECT(tfq_e4m3fn_encode_f32(f, p, 6, NULL) == TFQ_ERR_BAD_SHAPE);      /* n % 4 */
+    int32_t kern = -1, band = -1;
+    tfq_autotune_clear();
+    EXPECT(tfq_autotune_lookup(0, 256, 256, 256, 0, 0, &kern, &band) == 0); /* nothing cached */
+    EXPECT(tfq_last_hip_error() == 0);
 
     if (fails == 0) printf("c client ok: %zu entry points, ABI %d\n",
                            sizeof entry_points / sizeof entry_points[0], tfq_abi_version());
