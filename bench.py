@@ -174,6 +174,26 @@ def sample_sclk(torch, fn, seconds=3.0):
             "during": "the up GEMM + GELU run back to back for 3 s (amd-smi, mean over 8 XCDs)"}
 
 
+def quality_report(torch, x, w_up, w_dn, g, y, rows):
+    """E_max / E_rel of the quantised step's outputs on the first `rows`
+    tokens against FP32 GEMMs of the unquantised BF16 operands."""
+    def gelu_tanh(t):
+        return 0.5 * t * (1.0 + torch.tanh(0.7978845608028654 * (t + 0.044715 * t * t * t)))
+
+    def measures(got, ref):
+        d = (got.double() - ref.double())
+        return {"E_max": float(d.abs().max()), "E_rel": float(d.norm() / ref.double().norm())}
+
+    xr = x[:rows].float()
+    g_ref = gelu_tanh(xr @ w_up.float().t().contiguous())
+    y_ref = g_ref.bfloat16().float() @ w_dn.float().t().contiguous()
+    out = {"rows": rows, "reference": "FP32 GEMMs of the unquantised BF16 operands",
+           "up_gelu": measures(g[:rows].float(), g_ref), "pair": measures(y[:rows].float(), y_ref)}
+    del xr, g_ref, y_ref
+    torch.cuda.empty_cache()
+    return out
+
+
 def extras(torch, tfq, synth, stream):
     """Secondary workloads, each timed on its own (median of 20 after 5 warmup)."""
     out = {}
@@ -507,6 +527,12 @@ def main():
         kernels[kk]["config"] = None if cfg is None else {"kernel": cfg[0], "band": cfg[1]}
     log(f"step {ms_step:.3f} ms -> {value:.1f} TFLOP/s; per kernel {json.dumps(per)}")
 
+    # operator error against the unquantised product, E_max = max|y_q - y| and
+    # E_rel = ||y_q - y|| / ||y|| (TeleFuser "Quantization", "Validation"), on
+    # the first rows of the step just timed (qmax 448); the reference is two
+    # FP32 GEMMs of the BF16 inputs (GELU-tanh between them)
+    quality = quality_report(torch, x, w_up, w_dn, g, y, rows=2048)
+
     # the reduced-qmax sweep: same work, one timed step each
     sweep = {}
     for q in (14.0, 7.0):
@@ -570,6 +596,7 @@ def main():
                    "frac_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "quality": quality,
         "kernels": kernels,
         "qmax_sweep": sweep,
         "extras": ext,
