@@ -316,6 +316,8 @@ def mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, bits=8):
     step = ms_qx + ms_up + ms_qg + ms_dn
     out["step_ms_sum_of_medians"] = step
     out["step_tflops"] = 4.0 * M * N * K / step / 1e9
+    # g and y now hold this format's up and down outputs
+    out["quality"] = quality_report(torch, x, w_up, w_dn, g, y, rows=2048)
     return out
 
 
