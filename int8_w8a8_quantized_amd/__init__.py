@@ -467,7 +467,8 @@ class QuantLinear:
     (TeleFuser "Quantization", "tf-kernel FP8: online W8A8").  qtype "mxfp8",
     "mxfp6_e2m3", "mxfp6_e3m2" or "mxfp4" uses the MX formats instead
     (32-element blocks with E8M0 scales, weight and activations alike;
-    TeleFuser "Quantization", converter section)."""
+    TeleFuser "Quantization", converter section).  The weight codes are
+    cached: after changing the weight in place, call requantize()."""
 
     MX = {"mxfp8": (tfq_quantize_mx, tfq_scaled_mm_mxfp8),
           "mxfp4": (tfq_quantize_mxfp4, tfq_scaled_mm_mxfp4),
@@ -492,6 +493,12 @@ class QuantLinear:
         self.w_scale = None
         self._ws = None
         self._act = None
+
+    def requantize(self) -> None:
+        """Drop the cached weight codes and scales: the next call quantises
+        the current weight again (after the weight tensor was modified)."""
+        self.w_q = None
+        self.w_scale = None
 
     def quantized_weight(self):
         if self.w_q is None:

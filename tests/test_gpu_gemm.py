@@ -227,6 +227,14 @@ def test_quant_linear_module_caches_weight(tfq):
     torch.cuda.synchronize()
     assert lin.w_q is wq_first
     assert torch.equal(y1, y2)
+    # a changed weight is used only after requantize()
+    lin.weight.mul_(2.0)
+    y3 = lin(dev_bf16(xb))
+    lin.requantize()
+    y4 = lin(dev_bf16(xb))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y3)
+    assert lin.w_q is not wq_first and not torch.equal(y1, y4)
 
 
 def _sample_rows(M):
