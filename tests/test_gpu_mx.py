@@ -90,7 +90,8 @@ def _mx_operands(seed, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (300, 520, 384), (257, 264, 1152), (513, 768, 2048),
-                                   (64, 2048, 256)])
+                                   (64, 2048, 256),
+                                   (258, 136, 640), (259, 264, 384)])
 def test_mxfp8_gemm(tfq, M, N, K):
     _, _, qa, sa, qb, sb, bias = _mx_operands(M + 2 * N + K, M, N, K)
     a, b, sad, sbd = dev_u8(qa), dev_u8(qb), dev_u8(grouped(sa)), dev_u8(grouped(sb))

@@ -83,7 +83,8 @@ def _operands(seed, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (300, 520, 384), (257, 264, 1152), (513, 768, 2048),
-                                   (64, 2048, 256), (130, 136, 640)])
+                                   (64, 2048, 256), (130, 136, 640),
+                                   (258, 136, 640), (259, 264, 384)])
 def test_mxfp4_gemm(tfq, M, N, K):
     _, _, qa, sa, qb, sb, bias = _operands(M + 3 * N + K, M, N, K)
     a, b = dev_u8(qa), dev_u8(qb)
