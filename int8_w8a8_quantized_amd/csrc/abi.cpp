@@ -311,7 +311,9 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
     if (!qtype_ok(qtype) || !epi_ok(epi) || (scale_block != 0 && scale_block != 128) ||
         (scale_block == 128 && qtype != TFQ_QTYPE_E4M3FN))
         return TFQ_ERR_UNSUPPORTED;
-    if (m < 1 || m > kMaxDim || k < 16 || k % 16 != 0 || ld_x < k || ld_x > kMaxDim)
+    // (k bounded before workspace_bytes multiplies it by m)
+    if (m < 1 || m > kMaxDim || k < 16 || k > kMaxDim || k % 16 != 0 || ld_x < k ||
+        ld_x > kMaxDim)
         return TFQ_ERR_BAD_SHAPE;
     if (scale_block == 128 && k % 128 != 0) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(workspace, 256)) return TFQ_ERR_MISALIGNED;
@@ -486,8 +488,8 @@ tfq_status tfq_kv_cache_store(const void* kv_bf16, int64_t tokens, int64_t heads
     if (tokens < 1 || tokens > kMaxDim || heads < 1 || heads > 65536 || head_dim < 8 ||
         head_dim > 512 || head_dim % 8 != 0 || slots < 1 || slots > kMaxDim ||
         ld_token < heads * head_dim || ld_token > ((int64_t)1 << 40) || tokens * heads > kMaxDim ||
-        slots * heads > kMaxDim)
-        return TFQ_ERR_BAD_SHAPE;
+        slots * heads > kMaxDim || tokens - 1 > ((int64_t)1 << 61) / ld_token)
+        return TFQ_ERR_BAD_SHAPE;  // (the last bound keeps the input's byte span in range)
     if (ld_token % 8 != 0 || !aligned(kv_bf16, 16) || !aligned(cache, 16) ||
         !aligned(cache_scale, 4) || !aligned(slot_index, 4))
         return TFQ_ERR_MISALIGNED;

@@ -196,6 +196,7 @@ def test_kv_cache_validation(L):
     assert st(A, 4, 2, 520, 1040, B, 10, 448.0, C, D, None) == SHAPE   # head_dim > 512
     assert st(A, 4, 2, 128, 200, B, 10, 448.0, C, D, None) == SHAPE    # ld < heads * head_dim
     assert st(A, 4, 2, 128, 260, B, 10, 448.0, C, D, None) == ALIGN    # ld % 8
+    assert st(A, 1 << 30, 1, 8, 1 << 40, B, 10, 448.0, C, D, None) == SHAPE  # kv span > 2^61 bytes
     assert st(A, 4, 2, 128, 256, B, 10, 448.0, C + 8, D, None) == ALIGN
     assert st(A, 4, 2, 128, 256, B + 2, 10, 448.0, C, D, None) == ALIGN
     assert st(A, 4, 2, 128, 256, B, 10, 500.0, C, D, None) == QMAX
@@ -233,6 +234,10 @@ def test_fused_validation(L):
     assert fu(A, 100, 256, 256, B, C, 64, 1, 127.0, 128, None, 0, D, E, need, None) == UNSUP
     assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, A, need, None) == ALIAS
     assert fu(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, A + 256, E, need, None) == ALIAS
+    # K far past every limit is refused before the workspace size (m * k) is formed
+    big = 1 << 60
+    assert fu(A, 100, big, big, B, C, 64, 0, 448.0, 0, None, 0, D, E, need, None) == SHAPE
+    assert ws(100, big, 0, 0) == 0
 
 
 @no_gpu_only
