@@ -147,7 +147,8 @@ tfq_status tfq_quantize_weight_per_channel(const void* w_bf16, int64_t n, int64_
  *   scale_block 128: a_scale [m, k/128] (1x128 groups), b_scale [n/128, k/128]
  *                    (128x128 blocks); k % 128 == 0, n % 128 == 0,
  *                    k <= 131072 (else TFQ_ERR_BAD_SHAPE).
- *   bias_bf16  [n] BF16 or NULL, added after scaling (before GELU).
+ *   bias_bf16  [n] BF16 or NULL (16-byte aligned), added after scaling
+ *              (before GELU).
  *   epi        tfq_epilogue.
  *   y_bf16     [m, n] BF16, 16-byte aligned.
  *   m >= 1; n >= 8, n % 8 == 0; k >= 16, k % 16 == 0.
@@ -163,7 +164,7 @@ tfq_status tfq_scaled_mm_fp8(const uint8_t* a_q, const float* a_scale, const uin
  * weights.
  *
  *   a_q [m, k], b_q [n, k] int8 codes, 16-byte aligned; a_scale [m],
- *   b_scale [n]; bias_bf16 [n] or NULL; epi tfq_epilogue.
+ *   b_scale [n]; bias_bf16 [n] or NULL (16-byte aligned); epi tfq_epilogue.
  *   y_bf16  [m, n] BF16 output or NULL.
  *   acc_i32 [m, n] raw INT32 accumulators or NULL (16-byte aligned).
  *   At least one of y_bf16 / acc_i32 must be given.
@@ -186,7 +187,7 @@ tfq_status tfq_scaled_mm_int8(const int8_t* a_q, const float* a_scale, const int
  *   a_q [m, k] E4M3FN codes, a_scale [m] (e.g. from
  *   tfq_quantize_rows_gather, rows sorted by expert).
  *   b_q [groups, n, k] codes, b_scale [groups, n] FP32, bias_bf16
- *   [groups, n] BF16 or NULL.
+ *   [groups, n] BF16 or NULL (16-byte aligned).
  *   group_offsets [groups + 1] int32 DEVICE array, 4-byte aligned, read by
  *   the kernel: non-decreasing, group_offsets[0] >= 0, group_offsets[groups]
  *   <= m.  Rows in no group are not written.  Offsets that break these rules
@@ -219,7 +220,8 @@ size_t tfq_quant_linear_workspace_bytes(int64_t m, int64_t k, int32_t qtype, int
  *   x_bf16 [m, k] (row stride ld_x) BF16 activations; w_q [n, k] codes and
  *   w_scale ([n], or [n/128, k/128] for scale_block 128) from
  *   tfq_quantize_weight_per_channel; qtype applies to both operands;
- *   act_qmax the activation qmax; bias_bf16 [n] or NULL; epi tfq_epilogue;
+ *   act_qmax the activation qmax; bias_bf16 [n] or NULL (16-byte aligned);
+ *   epi tfq_epilogue;
  *   block mode (scale_block = 128) is FP8 only;
  *   y_bf16 [m, n]; workspace of at least
  *   tfq_quant_linear_workspace_bytes(m, k, qtype, scale_block) bytes,
@@ -232,13 +234,6 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
                                   int32_t epi, void* y_bf16, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/*
- * The device's own E4M3FN encoder (round-to-nearest-even, saturating to
- * +-448, sign of zero kept) applied to n FP32 values: the cast of TeleFuser
- * "Quantization", "Scaled FP8 checkpoints: W8A8", exposed on its own so that
- * the conversion the quantiser uses can be checked over all binary32 inputs.
- *   x [n] FP32, q [n] codes, both 16-byte aligned; n >= 1, n % 4 == 0.
- */
 /*
  * MXFP8 quantisation: E4M3FN codes with one E8M0 scale byte per 32
  * consecutive elements of a row.  TeleFuser "Quantization", converter
@@ -275,8 +270,8 @@ tfq_status tfq_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64
  *   a_scale [k/128, m], b_scale [k/128, n] scale words in the layout
  *   tfq_quantize_mx writes, 4-byte aligned (byte 255, NaN in the MX format,
  *   gives unspecified results).
- *   bias_bf16 [n] BF16 or NULL; epi tfq_epilogue; y_bf16 [m, n] BF16,
- *   16-byte aligned.
+ *   bias_bf16 [n] BF16 or NULL (16-byte aligned); epi tfq_epilogue;
+ *   y_bf16 [m, n] BF16, 16-byte aligned.
  *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 4194304, k % 128 == 0;
  *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
  */
@@ -313,7 +308,8 @@ tfq_status tfq_quantize_mxfp4(const void* x_bf16, int64_t rows, int64_t cols, in
  *   a_q [m, k/2], b_q [n, k/2] packed E2M1 codes (as tfq_quantize_mxfp4
  *   writes them), 16-byte aligned; a_scale [k/128, m], b_scale [k/128, n]
  *   scale words as for tfq_scaled_mm_mxfp8.
- *   bias_bf16 [n] or NULL; epi tfq_epilogue; y_bf16 [m, n] BF16.
+ *   bias_bf16 [n] or NULL (16-byte aligned); epi tfq_epilogue; y_bf16
+ *   [m, n] BF16.
  *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 8388608, k % 128 == 0;
  *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
  */
@@ -420,6 +416,13 @@ int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32
 /* Forget every cached configuration. */
 void tfq_autotune_clear(void);
 
+/*
+ * The device's own E4M3FN encoder (round-to-nearest-even, saturating to
+ * +-448, sign of zero kept) applied to n FP32 values: the cast of TeleFuser
+ * "Quantization", "Scaled FP8 checkpoints: W8A8", exposed on its own so that
+ * the conversion the quantiser uses can be checked over all binary32 inputs.
+ *   x [n] FP32, q [n] codes, both 16-byte aligned; n >= 1, n % 4 == 0.
+ */
 tfq_status tfq_e4m3fn_encode_f32(const float* x, uint8_t* q, int64_t n, void* stream);
 
 /* Static, NUL-terminated description of a status code. */

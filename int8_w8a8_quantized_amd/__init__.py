@@ -51,6 +51,37 @@ def _stream(stream) -> int | None:
     return int(stream)
 
 
+def _torch_stream(stream):
+    """`stream` (a torch stream or a raw hipStream_t handle) as a torch stream."""
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _on_stream(fn):
+    """Run a wrapper with the caller's `stream` (when one is given) as torch's
+    current stream, so that every tensor the wrapper allocates -- outputs,
+    the fused call's workspace -- belongs to that stream in torch's caching
+    allocator: a block freed there is handed out again only to later work on
+    the same stream, never to another stream while the kernels still use it.
+    The kernels run on that stream either way."""
+    import functools
+    import inspect
+
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        bound = sig.bind_partial(*args, **kwargs)
+        st = bound.arguments.get("stream")
+        if st is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(_torch_stream(st)):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
@@ -113,6 +144,7 @@ def tfq_abi_version() -> int:
     return lib().tfq_abi_version()
 
 
+@_on_stream
 def tfq_quantize_rows(x: torch.Tensor, qtype="fp8", qmax: float = 448.0, group_cols: int = 0,
                       q_out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
                       stream=None):
@@ -136,6 +168,7 @@ def tfq_quantize_rows(x: torch.Tensor, qtype="fp8", qmax: float = 448.0, group_c
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_quantize_rows_gather(x: torch.Tensor, row_index: torch.Tensor, qtype="fp8",
                              qmax: float = 448.0, group_cols: int = 0, q_out=None, scale_out=None,
                              stream=None):
@@ -162,6 +195,7 @@ def tfq_quantize_rows_gather(x: torch.Tensor, row_index: torch.Tensor, qtype="fp
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_quantize_weight_per_channel(w: torch.Tensor, qtype="fp8", qmax: float = 448.0,
                                     block: int = 0, q_out=None, scale_out=None, stream=None):
     """Weights W [n, k] BF16 -> (codes [n, k], scales [n] or [n/128, k/128])."""
@@ -182,6 +216,7 @@ def tfq_quantize_weight_per_channel(w: torch.Tensor, qtype="fp8", qmax: float = 
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_scaled_mm_fp8(a_q, a_scale, b_q, b_scale, scale_block: int = 0, bias=None, epi=None,
                       y=None, stream=None):
     """y [m, n] BF16 = (a_q [m,k] . b_q [n,k]^T) scaled per row / column (or per block)."""
@@ -201,6 +236,7 @@ def tfq_scaled_mm_fp8(a_q, a_scale, b_q, b_scale, scale_block: int = 0, bias=Non
     return y
 
 
+@_on_stream
 def tfq_scaled_mm_int8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, want_y: bool = True,
                        want_acc: bool = False, y=None, acc=None, stream=None):
     """INT8 scaled GEMM; returns (y BF16 or None, acc INT32 or None)."""
@@ -222,6 +258,7 @@ def tfq_scaled_mm_int8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, want_y: 
     return y, acc
 
 
+@_on_stream
 def tfq_grouped_scaled_mm_fp8(a_q, a_scale, b_q, b_scale, group_offsets, bias=None, epi=None,
                               y=None, stream=None):
     """Grouped (MoE) FP8 GEMM: rows group_offsets[g]..group_offsets[g+1] of
@@ -248,6 +285,7 @@ def tfq_quant_linear_workspace_bytes(m: int, k: int, qtype="fp8", scale_block: i
     return int(lib().tfq_quant_linear_workspace_bytes(m, k, _qt(qtype), int(scale_block)))
 
 
+@_on_stream
 def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0,
                            scale_block: int = 0, bias=None, epi=None, y=None, workspace=None,
                            stream=None):
@@ -274,6 +312,7 @@ def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0
     return y
 
 
+@_on_stream
 def tfq_quantize_mx(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
     """MXFP8 quantisation of BF16 rows x [rows, cols] (row stride x.stride(0)):
     returns (E4M3FN codes [rows, cols], E8M0 scales as uint8
@@ -292,6 +331,7 @@ def tfq_quantize_mx(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_scaled_mm_mxfp8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None, stream=None):
     """y [m, n] BF16 from MXFP8 operands a_q [m, k], b_q [n, k] with E8M0
     block scales in the layout tfq_quantize_mx returns ([k/128, m, 4] and
@@ -311,6 +351,7 @@ def tfq_scaled_mm_mxfp8(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None,
     return y
 
 
+@_on_stream
 def tfq_kv_cache_store(kv: torch.Tensor, slot_index: torch.Tensor, cache: torch.Tensor,
                        cache_scale: torch.Tensor, qmax: float = 448.0, stream=None):
     """Quantise kv [tokens, heads, head_dim] BF16 (heads and head_dim
@@ -330,6 +371,7 @@ def tfq_kv_cache_store(kv: torch.Tensor, slot_index: torch.Tensor, cache: torch.
                                    _stream(stream)), "tfq_kv_cache_store")
 
 
+@_on_stream
 def tfq_kv_cache_load(cache: torch.Tensor, cache_scale: torch.Tensor, slot_index: torch.Tensor,
                       dtype=torch.bfloat16, out=None, stream=None):
     """Dequantised cache rows slot_index[i]: [n, heads, head_dim] in dtype
@@ -373,6 +415,7 @@ def tfq_autotune_clear() -> None:
     lib().tfq_autotune_clear()
 
 
+@_on_stream
 def tfq_quantize_mxfp4(x: torch.Tensor, q_out=None, scale_out=None, stream=None):
     """MXFP4 quantisation of BF16 rows x [rows, cols]: returns (packed E2M1
     codes uint8 [rows, cols/2], lower index in the low nibble; E8M0 scales
@@ -390,6 +433,7 @@ def tfq_quantize_mxfp4(x: torch.Tensor, q_out=None, scale_out=None, stream=None)
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_scaled_mm_mxfp4(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None, stream=None):
     """y [m, n] BF16 from MXFP4 operands a_q [m, k/2], b_q [n, k/2] (packed)."""
     m, k2 = _arg(a_q, "a_q", (torch.uint8,), shape=(None, None)).shape
@@ -407,6 +451,7 @@ def tfq_scaled_mm_mxfp4(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None,
     return y
 
 
+@_on_stream
 def tfq_quantize_mxfp6(x: torch.Tensor, fmt="e2m3", q_out=None, scale_out=None, stream=None):
     """MXFP6 quantisation of BF16 rows x [rows, cols] (fmt "e2m3" or "e3m2"):
     returns (codes uint8 [rows, 3 cols / 4], a 6-bit little-endian stream per
@@ -426,6 +471,7 @@ def tfq_quantize_mxfp6(x: torch.Tensor, fmt="e2m3", q_out=None, scale_out=None, 
     return q_out, scale_out
 
 
+@_on_stream
 def tfq_scaled_mm_mxfp6(a_q, a_scale, b_q, b_scale, fmt="e2m3", bias=None, epi=None, y=None,
                         stream=None):
     """y [m, n] BF16 from MXFP6 operands a_q [m, 3k/4], b_q [n, 3k/4]."""
@@ -448,6 +494,7 @@ def tfq_scaled_mm_mxfp6(a_q, a_scale, b_q, b_scale, fmt="e2m3", bias=None, epi=N
     return y
 
 
+@_on_stream
 def tfq_e4m3fn_encode_f32(x: torch.Tensor, q=None, stream=None):
     """The device's E4M3FN encoder over a float32 tensor (numel % 4 == 0)."""
     _arg(x, "x", _F32)

@@ -119,7 +119,7 @@ tfq_status validate_gemm(const void* a, const float* sa, const void* b, const fl
     const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
     if (tiles > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
-        (bias && !aligned(bias, 2)) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
+        (bias && !aligned(bias, 16)) || (y && !aligned(y, 16)) || (acc && !aligned(acc, 16)))
         return TFQ_ERR_MISALIGNED;
     const int64_t nsa = block == 128 ? m * (k / 128) : m;
     const int64_t nsb = block == 128 ? (n / 128) * (k / 128) : n;
@@ -275,7 +275,7 @@ tfq_status tfq_grouped_scaled_mm_fp8(const uint8_t* a_q, const float* a_scale, c
         return TFQ_ERR_BAD_SHAPE;
     if (((m + 255) / 256 + groups) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-        !aligned(group_offsets, 4) || (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        !aligned(group_offsets, 4) || (bias_bf16 && !aligned(bias_bf16, 16)) || !aligned(y_bf16, 16))
         return TFQ_ERR_MISALIGNED;
     const Range ry = range_of(y_bf16, m * n * 2);
     const Range ins[6] = {range_of(a_q, m * k), range_of(b_q, groups * n * k),
@@ -393,7 +393,7 @@ tfq_status tfq_scaled_mm_mxfp4(const uint8_t* a_q, const uint32_t* a_scale, cons
         return TFQ_ERR_BAD_SHAPE;
     if (((m + 255) / 256) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-        (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        (bias_bf16 && !aligned(bias_bf16, 16)) || !aligned(y_bf16, 16))
         return TFQ_ERR_MISALIGNED;
     const Range ry = range_of(y_bf16, m * n * 2);
     const Range ins[5] = {range_of(a_q, m * k / 2), range_of(b_q, n * k / 2),
@@ -439,7 +439,7 @@ tfq_status tfq_scaled_mm_mxfp6(const uint8_t* a_q, const uint32_t* a_scale, cons
         return TFQ_ERR_BAD_SHAPE;
     if (((m + 255) / 256) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-        (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        (bias_bf16 && !aligned(bias_bf16, 16)) || !aligned(y_bf16, 16))
         return TFQ_ERR_MISALIGNED;
     const Range ry = range_of(y_bf16, m * n * 2);
     const Range ins[5] = {range_of(a_q, m * (k / 4 * 3)), range_of(b_q, n * (k / 4 * 3)),
@@ -466,7 +466,7 @@ tfq_status tfq_scaled_mm_mxfp8(const uint8_t* a_q, const uint32_t* a_scale, cons
         return TFQ_ERR_BAD_SHAPE;
     if (((m + 255) / 256) * ((n + 255) / 256) > INT32_MAX) return TFQ_ERR_BAD_SHAPE;
     if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-        (bias_bf16 && !aligned(bias_bf16, 2)) || !aligned(y_bf16, 16))
+        (bias_bf16 && !aligned(bias_bf16, 16)) || !aligned(y_bf16, 16))
         return TFQ_ERR_MISALIGNED;
     const Range ry = range_of(y_bf16, m * n * 2);
     const Range ins[5] = {range_of(a_q, m * k), range_of(b_q, n * k), range_of(a_scale, m * (k / 32)),

@@ -15,12 +15,16 @@
 //    (non-negative finite floats order like integers) using packed 16-bit
 //    max, then reduced with DPP row operations and four readlanes;
 //  * x / s is evaluated as q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0)
-//    with r = RN(1/s) (Markstein's correction step).  For s >= 2^-90 this
-//    equals the correctly rounded quotient whenever |x/s| >= 2^-12 (checked
-//    exhaustively over every BF16 amax / BF16 x pair for the qmax values the
-//    ABI accepts); smaller quotients encode to zero either way and the sign
-//    is restored from x.  Rows with s < 2^-90 or s > 2^126 (including an
-//    overflowed s = inf, where x / s = +-0) use a true division.
+//    with r = RN(1/s) (Markstein's correction step).  For 2^-90 <= s <=
+//    2^126 this equals the correctly rounded quotient whenever |x/s| >=
+//    2^-12, and smaller quotients encode to zero either way (the sign is
+//    restored from x): checked on the host for every BF16 amax and every BF16
+//    x with |x| <= amax, both signs, at qmax 448, 14, 12, 7 and 127
+//    (tests/test_divide_exhaustive.py); Markstein's theorem (a correctly
+//    rounded reciprocal, a first quotient within one ulp, no underflow of the
+//    remainder) covers the other accepted qmax values.  Rows with s < 2^-90
+//    or s > 2^126 (including an overflowed s = inf, where x / s = +-0) use a
+//    true division.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

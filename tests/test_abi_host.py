@@ -100,11 +100,16 @@ def test_gemm_validation(L):
     assert f(A, B, C, D, 64, 128, 131072 + 128, 128, None, 0, E, None) == SHAPE  # block-mode k bound
     assert f(A, B, C, D, 64, 64, 64, 0, None, 5, E, None) == UNSUP  # epilogue
     assert f(A + 4, B, C, D, 64, 64, 64, 0, None, 0, E, None) == ALIGN
+    # the bias is fetched with 16-byte loads: a 2-byte-aligned slice is refused
+    assert f(A, B, C, D, 64, 64, 64, 0, F + 2, 0, E, None) == ALIGN
+    assert f(A, B, C, D, 64, 128, 128, 128, F + 8, 0, E, None) == ALIGN
+    assert f(A, B, C, D, 64, 64, 64, 0, F + 16, 0, E, None) in (DEV, HIP)
     assert f(A, B, C, D, 64, 64, 64, 0, None, 0, A + 16, None) == ALIAS
     i = L.tfq_scaled_mm_int8
     assert i(A, B, C, D, 64, 64, 64, None, 0, None, None, None) == NULL
     assert i(A, B, C, D, 64, 64, 131072, None, 0, E, None, None) == SHAPE  # INT32 bound
     assert i(A, B, C, D, 64, 64, 64, None, 0, E, E + 64, None) == ALIAS    # y over acc
+    assert i(A, B, C, D, 64, 64, 64, F + 2, 0, E, None, None) == ALIGN     # bias alignment
 
 
 @no_gpu_only

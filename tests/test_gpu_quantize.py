@@ -142,3 +142,33 @@ def test_device_e4m3fn_encoder_every_binary32(tfq):
                 raise AssertionError(f"pattern {hb[i]:#010x}: gpu {got[i]:#x} oracle {ref[i]:#x}")
         del pos
     _ = lib
+
+
+@pytest.mark.parametrize("qtype,qmax", [("fp8", 448.0), ("int8", 127.0)])
+def test_every_bf16_pair_division(tfq, qtype, qmax):
+    """Every positive finite BF16 amax with every BF16 x, |x| <= amax: row j
+    holds amax_j and all BF16 magnitudes up to it (signs alternating), so the
+    kernel's division x / s runs on every (amax, x) pair; codes and scales
+    must equal the oracle's (true binary32 division) bit for bit."""
+    top = 0x7F7F  # largest finite BF16 magnitude
+    per = 1024
+    for lo in range(1, top + 1, per):
+        ab = np.arange(lo, min(lo + per, top + 1), dtype=np.int64)
+        width = int(-(-(int(ab[-1]) + 1) // 16) * 16)
+        col = np.arange(width, dtype=np.int64)
+        inside = col[None, :] <= ab[:, None]
+        sign = ((col[None, :] + ab[:, None]) & 1) << 15
+        x = np.where(inside, col[None, :] | sign, 0).astype(np.uint16)
+        say(f"every-pair division {qtype} qmax={qmax} amax bits [{lo:#06x}, {int(ab[-1]):#06x}] "
+            f"cols={width}")
+        xd = dev_bf16(x)
+        q, s = tfq.tfq_quantize_rows(xd, qtype, qmax)
+        torch.cuda.synchronize()
+        qe, se = orc.quantize_rows(x, qtype, qmax)
+        qg, sg = host_bits(q), host_bits(s)
+        assert np.array_equal(sg.view(np.uint32), se.view(np.uint32)), f"scales differ from {lo:#x}"
+        if not np.array_equal(qg, qe):
+            r, c = np.argwhere(qg != qe)[0]
+            raise AssertionError(f"codes differ: amax {int(ab[r]):#06x} x {x[r, c]:#06x}: "
+                                 f"gpu {qg[r, c]:#x} oracle {qe[r, c]:#x}")
+        del xd, q, s
