@@ -194,6 +194,20 @@ def quality_report(torch, x, w_up, w_dn, g, y, rows):
     return out
 
 
+def quality_linear(torch, x, w, y, rows, gelu=False):
+    """E_max / E_rel (TeleFuser "Quantization", "Validation") of a quantised
+    Linear's BF16 output y on the first `rows` rows against the FP32 GEMM of
+    the unquantised BF16 operands (GELU-tanh after it when gelu)."""
+    r = min(rows, x.shape[0])
+    ref = x[:r].float() @ w.float().t().contiguous()
+    if gelu:
+        ref = 0.5 * ref * (1.0 + torch.tanh(0.7978845608028654 * (ref + 0.044715 * ref ** 3)))
+    d = y[:r].double() - ref.double()
+    out = {"rows": r, "E_max": float(d.abs().max()), "E_rel": float(d.norm() / ref.double().norm())}
+    del ref, d
+    return out
+
+
 def extras(torch, tfq, synth, stream):
     """Secondary workloads, each timed on its own (median of 20 after 5 warmup)."""
     out = {}
@@ -211,7 +225,8 @@ def extras(torch, tfq, synth, stream):
         x, wq, ws, "fp8", 448.0, 0, None, None, y, wsp))
     fl = 2.0 * M * N * K
     out["c3_image_dit_fused_linear"] = {"ms": med, "ms_min": best, "tflops": fl / med / 1e9,
-                                        "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS}
+                                        "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS,
+                                        "quality": quality_linear(torch, x, w, y, 2048)}
     qa, sa = tfq.tfq_quantize_rows(x, "fp8", 448.0)
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 0, qa, sa))
     gbs = quant_bytes(M, K) / med / 1e6
@@ -250,7 +265,8 @@ def extras(torch, tfq, synth, stream):
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, 128, None,
                                                                       None, y))
     out["c5_block_gemm"] = {"ms": med, "tflops": fl / med / 1e9,
-                            "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS}
+                            "frac_fp8_peak": fl / med / 1e9 / FP8_PEAK_TFLOPS,
+                            "quality": quality_linear(torch, x, w, y, 2048)}
     del x, w, wq, ws, y, qa, sa
 
     # INT8
@@ -275,7 +291,16 @@ def extras(torch, tfq, synth, stream):
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_scaled_mm_int8(qa, sa, wq, ws, None, None,
                                                                        True, False, y))
     out["c2_int8_gemm"] = {"ms": med, "tops": fl / med / 1e9,
-                           "frac_int8_peak": fl / med / 1e9 / INT8_PEAK_TOPS}
+                           "frac_int8_peak": fl / med / 1e9 / INT8_PEAK_TOPS,
+                           "quality": quality_linear(torch, x, w, y, 2048)}
+    del x, w, wq, ws, y, qa, sa
+
+    # the tiny FP8 Linear (parity workload; quality only, it is launch-bound)
+    d = synth.make("c1_tiny_fp8")
+    x, w = dev_bf16(d["x"], torch), dev_bf16(d["w"], torch)
+    wq, ws = tfq.tfq_quantize_weight_per_channel(w, "fp8", 448.0)
+    y = tfq.tfq_quant_linear_fused(x, wq, ws, "fp8", 448.0)
+    out["c1_tiny_fp8"] = {"quality": quality_linear(torch, x, w, y, 128)}
     return out
 
 
@@ -416,6 +441,65 @@ def cpu_baseline(d, rows_sample: int):
     return flops / sec / 1e12, sec, orc.num_threads()
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_per_config(synth, d_c4, g_host):
+    """The oracle on the host cores for every workload: the quantiser at full
+    size (X of each workload, and the video-DiT G), GB/s over the same
+    algorithmic bytes as the GPU; the Linear on all rows of the tiny and INT8
+    workloads and on a 32-row sample of the image-DiT and block-scaled ones
+    (seconds for the sample and the linear extrapolation to all rows).  About
+    10-15 s on 16 host cores."""
+    import oracle as orc
+
+    out = {"quantize": {}, "linear": {}}
+
+    def tq(name, bits, qtype, qmax, group=0):
+        t0 = time.perf_counter()
+        res = orc.quantize_rows(bits, qtype, qmax, group)
+        sec = time.perf_counter() - t0
+        m, k = bits.shape
+        out["quantize"][name] = {"gbs": round(quant_bytes(m, k, group) / sec / 1e9, 3),
+                                 "seconds": round(sec, 3), "sample": f"full [{m}, {k}]"}
+        return res
+
+    tq("c4_video_dit_x", d_c4["x"], "fp8", 448.0)
+    if g_host is not None:
+        tq("c4_video_dit_g", g_host, "fp8", 448.0)
+    for wl, qt, qmax, grp, rows in (("c1_tiny_fp8", "fp8", 448.0, 0, None),
+                                    ("c2_int8", "int8", 127.0, 0, None),
+                                    ("c3_image_dit", "fp8", 448.0, 0, 32),
+                                    ("c5_block_fp8", "fp8", 448.0, 128, 32)):
+        d = synth.make(wl)
+        qa, sa = tq(wl + "_x", d["x"], qt, qmax, grp)
+        if grp:
+            qw, sw = orc.quantize_blocks(d["w"], qt, qmax, grp)
+        else:
+            qw, sw = orc.quantize_rows(d["w"], qt, qmax)
+        M, K, N = d["spec"].M, d["spec"].K, d["spec"].N
+        sel = None if rows is None else np.arange(rows)
+        t0 = time.perf_counter()
+        if qt == "int8":
+            orc.int8_linear(qa, sa, qw, sw, rows=sel)
+        else:
+            orc.linear_ref(qa, sa, qw, sw, "fp8", grp, rows=sel)
+        sec = time.perf_counter() - t0
+        r = M if rows is None else rows
+        out["linear"][wl] = {"tflops": round(2.0 * r * N * K / sec / 1e12, 6), "seconds": round(sec, 3),
+                             "sample": f"{r} of {M} rows" + (" (all)" if r == M else ""),
+                             "seconds_all_rows_extrapolated": round(sec * M / r, 1)}
+        del d, qa, sa, qw, sw
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -507,6 +591,8 @@ def main():
 
     per = {k: float(np.mean(timer.ms(k))) for k in ("quant_x", "gemm_up_gelu", "quant_g",
                                                        "gemm_down")}
+    # (the oracle's quantiser is timed on this G at the end)
+    g_host = None if args.no_cpu else g.view(torch.int16).cpu().numpy().view(np.uint16)
     up_flops = 2.0 * M * N * K
     achieved = up_flops / (per["gemm_up_gelu"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "scaled_gemm fp8 (up projection + GELU epilogue)",
@@ -535,16 +621,22 @@ def main():
     # FP32 GEMMs of the BF16 inputs (GELU-tanh between them)
     quality = quality_report(torch, x, w_up, w_dn, g, y, rows=2048)
 
-    # the reduced-qmax sweep: same work, one timed step each
+    # the reduced-qmax sweep (LightX2V "模型量化技术", "MiniMax-H3 FP8 FP16
+    # 累加"): the same step at activation qmax 14 and 7, 3 timed steps each,
+    # with per-kernel times and the operator error of each
     sweep = {}
     for q in (14.0, 7.0):
         step(q)
         torch.cuda.synchronize()
+        timer.clear()
         t1 = time.perf_counter()
         for _ in range(3):
             step(q)
         torch.cuda.synchronize()
-        sweep[str(q)] = {"ms_per_step": (time.perf_counter() - t1) * 1e3 / 3}
+        per_q = {k: float(np.mean(timer.ms(k))) for k in ("quant_x", "gemm_up_gelu", "quant_g",
+                                                            "gemm_down")}
+        sweep[str(q)] = {"ms_per_step": (time.perf_counter() - t1) * 1e3 / 3, "kernels_ms": per_q,
+                         "quality": quality_report(torch, x, w_up, w_dn, g, y, rows=2048)}
     timer.clear()
     sclk = None
     if not args.no_clock:
@@ -576,8 +668,19 @@ def main():
         tf, sec, thr = cpu_baseline(d, args.cpu_rows)
         cpu = {"value": round(tf, 6), "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
                "sample": f"{args.cpu_rows} of {M} token rows of the FFN-pair step (quantise X, "
-                         f"up GEMM + GELU, quantise G, down GEMM), {sec:.1f} s"}
+                         f"up GEMM + GELU, quantise G, down GEMM), {sec:.1f} s; all {M} rows "
+                         f"extrapolated: {sec * M / args.cpu_rows:.0f} s",
+               "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+        log("cpu baseline: oracle per workload (quantisers at full size, Linear samples)")
+        cpu["per_config"] = cpu_baseline_per_config(synth, d, g_host)
 
+    # operator error by workload and activation qmax
+    all_quality = {"c4_video_dit": {str(args.qmax): quality,
+                                    **{k: v["quality"] for k, v in sweep.items()}}}
+    for key, wl in (("c3_image_dit_fused_linear", "c3_image_dit"), ("c5_block_gemm", "c5_block_fp8"),
+                    ("c2_int8_gemm", "c2_int8"), ("c1_tiny_fp8", "c1_tiny_fp8")):
+        if key in ext and "quality" in ext[key]:
+            all_quality[wl] = {"448.0" if wl != "c2_int8" else "127.0": ext[key]["quality"]}
     out = {
         "metric": "FP8 W8A8 Linear TFLOP/s (% FP8 MFMA peak) + quantize GB/s at DiT shapes",
         "value": round(value, 2),
@@ -598,7 +701,7 @@ def main():
                    "frac_fp8_peak": round(value / FP8_PEAK_TFLOPS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "quality": quality,
+        "quality": all_quality,
         "kernels": kernels,
         "qmax_sweep": sweep,
         "extras": ext,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 7
+#define TFQ_ABI_VERSION 8
 
 typedef enum tfq_status {
     TFQ_OK = 0,
@@ -404,14 +404,26 @@ tfq_status tfq_set_autotune(int32_t mode);
 /*
  * The cached configuration of a shape, if any: returns 1 and writes kernel
  * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU) and band (tile rows per
- * band of the tile order), else 0.  kind: 0 FP8 per channel
- * (tfq_scaled_mm_fp8, scale_block 0, and the fused FP8 Linear), 1 INT8,
- * 2 FP8 block-scaled, 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4,
- * 6 MXFP6 E2M3, 7 MXFP6 E3M2.  Looks up the
- * current device's entries.
+ * band of the tile order), else 0.  kind: 0 FP8 per channel (tfq_scaled_mm_fp8,
+ * scale_block 0, and the fused FP8 Linear), 1 INT8, 2 FP8 block-scaled,
+ * 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4, 6 MXFP6 E2M3, 7 MXFP6
+ * E3M2.  Looks up the current device's entries.
  */
 int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
                             int32_t groups, int32_t* kernel, int32_t* band);
+
+/*
+ * Put a launch configuration for one shape into the current device's cache
+ * (the same cache tuning fills, with the same key as tfq_autotune_lookup):
+ * a tuning table saved from an earlier run can be loaded this way instead of
+ * tuning again.  The configuration is used while autotuning is on
+ * (tfq_set_autotune(1)).  It must be one of the configurations the tuner
+ * would try for that shape, all of which give the same result bits;
+ * otherwise TFQ_ERR_UNSUPPORTED (also for an unknown kind or epilogue).
+ * TFQ_ERR_BAD_SHAPE for non-positive sizes or groups outside 1..256 (kind 4).
+ */
+tfq_status tfq_autotune_set(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
+                            int32_t groups, int32_t kernel, int32_t band);
 
 /* Forget every cached configuration. */
 void tfq_autotune_clear(void);

@@ -22,10 +22,11 @@ from ._lib import TfqError, check, lib
 __all__ = [
     "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
-    "tfq_quant_linear_fused", "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
+    "tfq_quant_linear_fused",
+    "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
     "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
     "tfq_kv_cache_load", "KV_DTYPE", "tfq_set_autotune", "tfq_autotune_lookup",
-    "tfq_autotune_clear", "tfq_quantize_mxfp4", "tfq_scaled_mm_mxfp4", "tfq_quantize_mxfp6",
+    "tfq_autotune_clear", "tfq_autotune_set", "tfq_quantize_mxfp4", "tfq_scaled_mm_mxfp4", "tfq_quantize_mxfp6",
     "tfq_scaled_mm_mxfp6", "FP6",
     "tfq_abi_version", "QuantLinear",
 ]
@@ -413,6 +414,16 @@ def tfq_autotune_lookup(kind, m: int, n: int, k: int, epi=None, groups: int = 0)
 
 def tfq_autotune_clear() -> None:
     lib().tfq_autotune_clear()
+
+
+def tfq_autotune_set(kind, m: int, n: int, k: int, kernel: int, band: int, epi=None,
+                     groups: int = 0) -> None:
+    """Cache launch configuration (kernel, band) for a GEMM shape on the
+    current device, as tuning would (used while autotuning is on); it must be
+    one of the shape's candidate configurations."""
+    kd = AUTOTUNE_KIND[kind] if isinstance(kind, str) else int(kind)
+    check(lib().tfq_autotune_set(kd, m, n, k, _epi(epi), int(groups), int(kernel), int(band)),
+          "tfq_autotune_set")
 
 
 @_on_stream

@@ -540,8 +540,9 @@ tfq_status tfq_set_autotune(int32_t mode)
     return TFQ_OK;
 }
 
-int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
-                            int32_t groups, int32_t* kernel, int32_t* band)
+// the GEMM kind codes of tfq_autotune_lookup / tfq_autotune_set
+static bool gemm_kind(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi, int32_t groups,
+                      tfq::GemmArgs* out)
 {
     tfq::GemmArgs g{};
     g.m = m;
@@ -557,8 +558,35 @@ int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32
     case 6: g.qtype = tfq::kMxE2M3; break;
     case 7: g.qtype = tfq::kMxE3M2; break;
     case 4: g.qtype = tfq::kE4M3FN; g.groups = groups; break;
-    default: return 0;
+    default: return false;
     }
+    *out = g;
+    return true;
+}
+
+tfq_status tfq_autotune_set(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi, int32_t groups,
+                            int32_t kernel, int32_t band)
+{
+    tfq::GemmArgs g{};
+    if (!gemm_kind(kind, m, n, k, epi, groups, &g) || !epi_ok(epi)) return TFQ_ERR_UNSUPPORTED;
+    if (kind == 4 && (groups < 1 || groups > 256)) return TFQ_ERR_BAD_SHAPE;
+    if (m < 1 || n < 1 || k < 1) return TFQ_ERR_BAD_SHAPE;
+    if (!tfq::config_is_candidate(g, tfq::GemmConfig{kernel, band})) return TFQ_ERR_UNSUPPORTED;
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return TFQ_ERR_UNSUPPORTED_DEVICE;
+    }
+    tfq::autotune_set(dev, g, tfq::GemmConfig{kernel, band});
+    return TFQ_OK;
+}
+
+int32_t tfq_autotune_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t epi,
+                            int32_t groups, int32_t* kernel, int32_t* band)
+{
+    tfq::GemmArgs g{};
+    if (!gemm_kind(kind, m, n, k, epi, groups, &g)) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();

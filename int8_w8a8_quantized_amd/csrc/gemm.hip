@@ -1254,6 +1254,15 @@ int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
     return n;
 }
 
+bool config_is_candidate(const GemmArgs& g, GemmConfig c)
+{
+    GemmConfig cand[16];
+    const int n = candidate_configs(g, cand, 16);
+    for (int i = 0; i < n; ++i)
+        if (cand[i].kernel == c.kernel && cand[i].band == c.band) return true;
+    return false;
+}
+
 // Every configuration sums every output in the same order (same MFMAs, same
 // K stages, only the tile order or tile shape differs), so the choice never
 // changes a result bit.

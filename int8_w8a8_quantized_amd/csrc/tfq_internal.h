@@ -70,7 +70,8 @@ struct GemmArgs {
 
 // A GEMM launch configuration: kernel 0 = 256x256 tiles, 1 = 256x128 tiles
 // two per CU (per-channel FP8 / INT8 only); band = tile rows per band of the
-// tile order.  Every configuration gives the same result bits.
+// tile order.  Every candidate configuration of a shape gives the same
+// result bits.
 struct GemmConfig {
     int kernel;
     int band;
@@ -79,6 +80,7 @@ struct GemmConfig {
 GemmConfig default_config(const GemmArgs& g);
 // the configurations the autotuner times for g (at most max_out)
 int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out);
+bool config_is_candidate(const GemmArgs& g, GemmConfig c);
 hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t stream);
 // the library's GEMM launch: the autotuned configuration if autotuning is on
 // (tune.cpp), else default_config
@@ -88,6 +90,8 @@ hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);
 void set_autotune(int mode);
 int autotune_mode();
 bool autotune_lookup(int dev, const GemmArgs& g, GemmConfig* out);
+// put c (a candidate of g) in the cache of device dev
+void autotune_set(int dev, const GemmArgs& g, GemmConfig c);
 void autotune_clear();
 
 }  // namespace tfq

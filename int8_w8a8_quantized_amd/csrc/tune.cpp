@@ -102,6 +102,12 @@ bool autotune_lookup(int dev, const GemmArgs& g, GemmConfig* out)
     return find(key_of(dev, g), out);
 }
 
+void autotune_set(int dev, const GemmArgs& g, GemmConfig c)
+{
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache[key_of(dev, g)] = c;
+}
+
 void autotune_clear()
 {
     std::lock_guard<std::mutex> lk(g_cache_mu);

@@ -105,6 +105,10 @@ def lib():
         L.tfq_oracle_quantize_mx4.argtypes = [P, i64, i64, i64, P, P]
         L.tfq_oracle_linear_mx4_ref.restype = None
         L.tfq_oracle_linear_mx4_ref.argtypes = [P, P, P, P, i64, i64, i64, P, ctypes.c_int, P, i64, P]
+        L.tfq_oracle_gelu_tanh_array.restype = None
+        L.tfq_oracle_gelu_tanh_array.argtypes = [P, i64]
+        L.tfq_oracle_int8_epilogue.restype = None
+        L.tfq_oracle_int8_epilogue.argtypes = [P, P, P, i64, i64, P, P, P]
         L.tfq_oracle_int8_linear.restype = None
         L.tfq_oracle_int8_linear.argtypes = [P, P, P, P, i64, i64, i64, P, P, i64, P, P]
         L.tfq_oracle_error_measures.restype = None
@@ -254,6 +258,82 @@ def linear_ref(a_q, a_scale, b_q, b_scale, qtype, scale_block: int = 0, bias=Non
                                 int(scale_block), _ptr(bi), 1 if gelu else 0, _ptr(r), nr,
                                 _ptr(out))
     return out
+
+
+def _code_values64(codes: np.ndarray, qtype) -> np.ndarray:
+    """Exact binary64 values of FP8 (E4M3FN) or INT8 codes."""
+    c = np.ascontiguousarray(codes).view(np.uint8)
+    if _qtype(qtype) == QTYPE_E4M3FN:
+        return e4m3fn_table()[c]
+    return c.view(np.int8).astype(np.float64)
+
+
+def linear_ref_fast(a_q, a_scale, b_q, b_scale, qtype, scale_block: int = 0, bias=None,
+                    gelu: bool = False, rows=None) -> np.ndarray:
+    """linear_ref with the dots formed by numpy's binary64 matmul (BLAS).
+
+    The exact-dot property makes this the same reference, bit for bit: every
+    E4M3FN or INT8 code value is an integer multiple of 2^-9 of magnitude at
+    most 448, so each product is a multiple of 2^-18 below 2^17.7 and any
+    partial sum of K <= 2^17 of them is exactly representable in binary64 --
+    in whatever order or blocking the library sums.  The scaling then follows
+    tfq_oracle_linear_ref's binary64 steps in its order: (dot * s_row) * s_col,
+    or sum over K blocks of (s_row[m,kb] * s_col[n/blk,kb]) * dot_kb in block
+    order; + bias; GELU-tanh by the C function.  Pinned bit-equal to
+    linear_ref in tests/test_oracle_gemm.py."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    M, K = a.shape
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    ar = _code_values64(a if r is None else a[r], qtype)
+    b64 = _code_values64(b_q, qtype)
+    N = b64.shape[0]
+    assert b64.shape[1] == K and K <= (1 << 17)
+    sa = np.ascontiguousarray(a_scale, dtype=np.float32).astype(np.float64)
+    sb = np.ascontiguousarray(b_scale, dtype=np.float32).astype(np.float64)
+    if scale_block <= 0:
+        s_row = sa if r is None else sa[r]
+        y = ((ar @ b64.T) * s_row[:, None]) * sb[None, :]
+    else:
+        blk = int(scale_block)
+        nkb = (K + blk - 1) // blk
+        sa2 = sa.reshape(M, nkb)
+        sb2 = sb.reshape(-1, nkb)
+        s_rows = sa2 if r is None else sa2[r]
+        y = np.zeros((ar.shape[0], N), dtype=np.float64)
+        nb_of = np.arange(N) // blk
+        for kb in range(nkb):
+            k0, k1 = kb * blk, min(K, (kb + 1) * blk)
+            d = ar[:, k0:k1] @ b64[:, k0:k1].T
+            y = y + (s_rows[:, kb][:, None] * sb2[nb_of, kb][None, :]) * d
+    if bias is not None:
+        bv = (np.ascontiguousarray(bias, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+        y = y + bv.astype(np.float64)[None, :]
+    y = np.ascontiguousarray(y)
+    if gelu:
+        lib().tfq_oracle_gelu_tanh_array(_ptr(y), y.size)
+    return y
+
+
+def int8_linear_fast(a_q, a_scale, b_q, b_scale, bias=None, rows=None):
+    """int8_linear with the integer sums formed by a binary64 matmul (exact:
+    |q| <= 128 so |sum| < 2^31 << 2^53 for K <= 131071) and the BF16
+    epilogue by the C function.  Returns (acc int64 [R,N], y bf16 bits [R,N]).
+    Pinned equal to int8_linear in tests/test_oracle_gemm.py."""
+    a = np.ascontiguousarray(a_q).view(np.uint8)
+    M, K = a.shape
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    ar = _code_values64(a if r is None else a[r], QTYPE_INT8)
+    b64 = _code_values64(b_q, QTYPE_INT8)
+    N = b64.shape[0]
+    assert b64.shape[1] == K and K <= 131071
+    acc = np.ascontiguousarray((ar @ b64.T).astype(np.int64))
+    sa = np.ascontiguousarray(a_scale, dtype=np.float32)
+    sb = np.ascontiguousarray(b_scale, dtype=np.float32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
+    y = np.empty(acc.shape, dtype=np.uint16)
+    lib().tfq_oracle_int8_epilogue(_ptr(acc), _ptr(sa), _ptr(sb), acc.shape[0], N, _ptr(bi),
+                                   _ptr(r), _ptr(y))
+    return acc, y
 
 
 def mx_scale_code(amax: float) -> int:

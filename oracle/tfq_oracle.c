@@ -706,6 +706,34 @@ void tfq_oracle_int8_linear(const int8_t* a, const float* a_scale, const int8_t*
     }
 }
 
+/* Array forms of two steps above, for references that form the exact dots
+ * with a library matmul (the exact-dot property: any binary64 summation
+ * order gives the same sum for K <= 2^17): GELU-tanh of n values in place,
+ * and the INT8 BF16 epilogue of tfq_oracle_int8_linear on given INT sums
+ * (sums [R, N] of rows `rows`, or of rows 0..R-1 when rows is NULL). */
+void tfq_oracle_gelu_tanh_array(double* v, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) v[i] = tfq_oracle_gelu_tanh(v[i]);
+}
+
+void tfq_oracle_int8_epilogue(const int64_t* sums, const float* a_scale, const float* b_scale,
+                              int64_t R, int64_t N, const uint16_t* bias, const int64_t* rows,
+                              uint16_t* y_bf16)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t n = 0; n < N; ++n) {
+            float f = (float)sums[i * N + n]; /* RN int -> binary32 */
+            f = f * a_scale[m];               /* RN */
+            f = f * b_scale[n];               /* RN */
+            if (bias) f = f + tfq_oracle_bf16_to_f32(bias[n]);
+            y_bf16[i * N + n] = tfq_oracle_f32_to_bf16(f);
+        }
+    }
+}
+
 /* Operator error measures of [TF-en] "Validation": E_max = max|y_q - y| and
  * E_rel = ||y_q - y||_2 / ||y||_2 over n values. */
 void tfq_oracle_error_measures(const double* yq, const double* y, int64_t n, double* e_max,

@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 7
+    assert L.tfq_abi_version() == 8
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
@@ -269,3 +269,19 @@ def test_python_binding_names_match_abi():
         if n in ("tfq_status_string", "tfq_last_hip_error"):
             continue
         assert callable(getattr(P, n)), n
+
+
+def test_autotune_set_validation(L):
+    s = L.tfq_autotune_set
+    assert s(9, 4096, 4096, 4096, 0, 0, 2, 4) == UNSUP       # unknown kind
+    assert s(0, 4096, 4096, 4096, 7, 0, 2, 4) == UNSUP       # unknown epilogue
+    assert s(0, 4096, 4096, 4096, 0, 0, 2, 4) == UNSUP       # no such kernel
+    assert s(0, 4096, 4096, 4096, 0, 0, 0, 3) == UNSUP       # band not a candidate
+    assert s(0, 4096, 8192, 4096, 0, 0, 1, 4) == UNSUP       # two-per-CU only below 512 tiles
+    assert s(2, 4096, 4096, 4096, 0, 0, 1, 4) == UNSUP       # block-scaled: kernel 0 only
+    assert s(4, 4096, 4096, 4096, 0, 0, 0, 4) == SHAPE       # grouped needs 1..256 groups
+    assert s(0, 0, 4096, 4096, 0, 0, 0, 4) == SHAPE
+    if not HAS_GPU_NODE:
+        # a valid candidate: only the missing device stops it
+        assert s(1, 4096, 4096, 4096, 0, 0, 1, 4) == DEV
+        assert s(0, 4096, 4096, 4096, 1, 0, 0, 8) == DEV

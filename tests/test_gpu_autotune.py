@@ -10,7 +10,7 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import dev_bf16, dev_f32, dev_u8, host_bits, needs_gpu, say
+from gpu_util import assert_fp8_tolerance, dev_bf16, dev_f32, dev_u8, host_bits, needs_gpu, say
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -46,6 +46,60 @@ def test_fp8_tuned_equals_default(tfq, M, N, K):
     cfg = tfq.tfq_autotune_lookup("fp8", M, N, K, "gelu_tanh")
     assert cfg is not None and cfg[0] in (0, 1) and cfg[1] in (1, 2, 4, 8)
     assert tfq.tfq_autotune_lookup("fp8", M, N, K, None) is None   # another key
+    # the tuned result against the oracle directly (sampled rows + the ragged tail)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
+                                     rng.integers(0, M, 32)]))
+    ref = orc.linear_ref(qa, sa, qb, sb, "fp8", gelu=True, rows=rows)
+    assert_fp8_tolerance(host_bits(y1)[rows], ref, "tuned fp8 + gelu")
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+def test_every_candidate_configuration(tfq, qtype):
+    """tfq_autotune_set pins each candidate configuration of a shape in turn
+    (the 256x256 and the two-per-CU 256x128 kernel, every band height): every
+    one writes the same bits, which match the oracle.  A configuration that
+    is not a candidate is refused."""
+    M, N, K = 777, 1000, 1040
+    rng = np.random.default_rng(17)
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.to_bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    qmax = 448.0 if qtype == "fp8" else 127.0
+    qa, sa = orc.quantize_rows(x, qtype, qmax)
+    qb, sb = orc.quantize_rows(w, qtype, qmax)
+    dt = torch.uint8 if qtype == "fp8" else torch.int8
+    a, b, sad, sbd = dev_u8(qa, dt), dev_u8(qb, dt), dev_f32(sa), dev_f32(sb)
+    kernels = (0, 1)
+    epi = "gelu_tanh" if qtype == "fp8" else None  # INT8: the bit-exact BF16 epilogue
+    tfq.tfq_set_autotune(1)
+    outs = {}
+    for kern in kernels:
+        for band in (1, 2, 4, 8):
+            say(f"pinned config {qtype} kernel={kern} band={band} M={M} N={N} K={K}")
+            tfq.tfq_autotune_set(qtype, M, N, K, kern, band, epi)
+            assert tfq.tfq_autotune_lookup(qtype, M, N, K, epi) == (kern, band)
+            if qtype == "fp8":
+                y = tfq.tfq_scaled_mm_fp8(a, sad, b, sbd, 0, None, epi)
+                outs[(kern, band)] = (host_bits(y),)
+            else:
+                y, acc = tfq.tfq_scaled_mm_int8(a, sad, b, sbd, None, epi, want_acc=True)
+                outs[(kern, band)] = (host_bits(y), host_bits(acc))
+            torch.cuda.synchronize()
+    first = next(iter(outs.values()))
+    for k, v in outs.items():
+        for got, want in zip(v, first):
+            assert np.array_equal(got, want), f"configuration {k} differs"
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.integers(0, M, 24)]))
+    if qtype == "fp8":
+        ref = orc.linear_ref(qa, sa, qb, sb, qtype, gelu=True, rows=rows)
+        assert_fp8_tolerance(first[0][rows], ref, "pinned configurations")
+    else:
+        acc_e, y_e = orc.int8_linear(qa, sa, qb, sb, rows=rows)
+        assert np.array_equal(first[1][rows].astype(np.int64), acc_e), "INT32 sums differ"
+        assert np.array_equal(first[0][rows], y_e), "INT8 BF16 output differs from the oracle"
+    with pytest.raises(tfq.TfqError):
+        tfq.tfq_autotune_set(qtype, M, N, K, 5, 4, epi)
+    with pytest.raises(tfq.TfqError):
+        tfq.tfq_autotune_set(qtype, M, N, K, 2, 3, epi)
 
 
 def test_other_kinds_tuned_equal_default(tfq):

@@ -179,3 +179,68 @@ def test_error_measures(orc):
     yq = np.array([3.0, -4.0, 0.5])
     emax, erel = orc.error_measures(yq, y)
     assert emax == 0.5 and erel == 0.1
+
+
+def _fp8_operands(rng, M, N, K, orc, qtype="fp8", wscale=0.02):
+    x = synth.to_bf16_bits((rng.standard_normal((M, K)) *
+                            np.exp2(rng.integers(-8, 8, (M, 1)))).astype(np.float32))
+    w = synth.to_bf16_bits((wscale * rng.standard_normal((N, K))).astype(np.float32))
+    qmax = 448.0 if qtype == "fp8" else 127.0
+    return orc.quantize_rows(x, qtype, qmax), orc.quantize_rows(w, qtype, qmax)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 16), (7, 40, 96), (33, 130, 520), (5, 24, 13824)])
+@pytest.mark.parametrize("gelu", [False, True])
+def test_fast_linear_ref_bit_equal_to_loop_version(orc, M, N, K, gelu):
+    """The BLAS-formed reference equals the loop reference bit for bit (the
+    exact-dot property), with and without bias and GELU, on all rows and on a
+    row selection; K = 13 824 is the video-DiT down projection."""
+    rng = np.random.default_rng(M * 1000 + K + gelu)
+    (qa, sa), (qb, sb) = _fp8_operands(rng, M, N, K, orc)
+    bias = synth.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    for b in (None, bias):
+        ref = orc.linear_ref(qa, sa, qb, sb, "fp8", bias=b, gelu=gelu)
+        fast = orc.linear_ref_fast(qa, sa, qb, sb, "fp8", bias=b, gelu=gelu)
+        assert np.array_equal(ref.view(np.uint64), fast.view(np.uint64))
+    rows = rng.integers(0, M, 5)
+    ref = orc.linear_ref(qa, sa, qb, sb, "fp8", gelu=gelu, rows=rows)
+    fast = orc.linear_ref_fast(qa, sa, qb, sb, "fp8", gelu=gelu, rows=rows)
+    assert np.array_equal(ref.view(np.uint64), fast.view(np.uint64))
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 128, 128), (9, 256, 640)])
+def test_fast_linear_ref_block_mode_bit_equal(orc, M, N, K):
+    rng = np.random.default_rng(N + K)
+    x = synth.to_bf16_bits((rng.standard_normal((M, K)) *
+                            np.exp2(rng.integers(-6, 6, (M, K // 128)).repeat(128, 1))
+                            ).astype(np.float32))
+    w = synth.to_bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    qa, sa = orc.quantize_rows(x, "fp8", 448.0, 128)
+    qb, sb = orc.quantize_blocks(w, "fp8", 448.0, 128)
+    bias = synth.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    for gelu in (False, True):
+        ref = orc.linear_ref(qa, sa, qb, sb, "fp8", 128, bias=bias, gelu=gelu)
+        fast = orc.linear_ref_fast(qa, sa, qb, sb, "fp8", 128, bias=bias, gelu=gelu)
+        assert np.array_equal(ref.view(np.uint64), fast.view(np.uint64))
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 16, 32), (17, 72, 3072)])
+def test_fast_int8_linear_equal_to_loop_version(orc, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    (qa, sa), (qb, sb) = _fp8_operands(rng, M, N, K, orc, "int8")
+    bias = synth.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    for b in (None, bias):
+        acc, y = orc.int8_linear(qa, sa, qb, sb, bias=b)
+        acc_f, y_f = orc.int8_linear_fast(qa, sa, qb, sb, bias=b)
+        assert np.array_equal(acc, acc_f) and np.array_equal(y, y_f)
+    rows = np.array([M - 1, 0, M // 2])
+    acc, y = orc.int8_linear(qa, sa, qb, sb, rows=rows)
+    acc_f, y_f = orc.int8_linear_fast(qa, sa, qb, sb, rows=rows)
+    assert np.array_equal(acc, acc_f) and np.array_equal(y, y_f)
+    # extreme codes at the INT32 bound: K = 131056 rows of -128 / 127 sums
+    qa2 = np.full((1, 131056), -128, dtype=np.int8).view(np.uint8)
+    qb2 = np.full((2, 131056), -128, dtype=np.int8)
+    qb2[1] = 127
+    one = np.ones(1, np.float32)
+    acc_f, _ = orc.int8_linear_fast(qa2, one, qb2.view(np.uint8), np.ones(2, np.float32))
+    assert acc_f.tolist() == [[128 * 128 * 131056, -128 * 127 * 131056]]
