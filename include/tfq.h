@@ -234,6 +234,35 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
                                   int32_t epi, void* y_bf16, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch of tfq_quant_linear_fused_noalloc (per GPU). */
+#define TFQ_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * tfq_quant_linear_fused for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same quantise + scaled GEMM kernels, with the activation
+ * codes and scales in a device array of TFQ_NOALLOC_WORKSPACE_BYTES that the
+ * library holds on each GPU it runs on until the process ends, instead of a
+ * caller workspace.  The call allocates nothing (no hipMalloc, no host or
+ * device allocation by any library it uses) and never tunes: it launches the
+ * GEMM configuration already cached for the shape (tfq_set_autotune) or the
+ * heuristic one.  Arguments as for tfq_quant_linear_fused without the
+ * workspace.
+ *
+ * Limit: tfq_quant_linear_workspace_bytes(m, k, qtype, scale_block) must not
+ * exceed TFQ_NOALLOC_WORKSPACE_BYTES, else TFQ_ERR_WORKSPACE_TOO_SMALL (e.g.
+ * 64 MiB holds m * k up to about 66e6 activation codes).
+ *
+ * Calls on one GPU share its array and each call leaves its codes there:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * give unspecified results; calls ordered on one stream are safe.
+ */
+tfq_status tfq_quant_linear_fused_noalloc(const void* x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                          const void* w_q, const float* w_scale, int64_t n,
+                                          int32_t qtype, float act_qmax, int32_t scale_block,
+                                          const void* bias_bf16, int32_t epi, void* y_bf16,
+                                          void* stream);
+
 /*
  * MXFP8 quantisation: E4M3FN codes with one E8M0 scale byte per 32
  * consecutive elements of a row.  TeleFuser "Quantization", converter

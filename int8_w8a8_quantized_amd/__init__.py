@@ -22,7 +22,7 @@ from ._lib import TfqError, check, lib
 __all__ = [
     "TfqError", "QTYPE", "EPI", "tfq_quantize_rows", "tfq_quantize_weight_per_channel",
     "tfq_scaled_mm_fp8", "tfq_scaled_mm_int8", "tfq_quant_linear_workspace_bytes",
-    "tfq_quant_linear_fused",
+    "tfq_quant_linear_fused", "tfq_quant_linear_fused_noalloc", "NOALLOC_WORKSPACE_BYTES",
     "tfq_quantize_mx", "tfq_scaled_mm_mxfp8", "tfq_e4m3fn_encode_f32",
     "tfq_quantize_rows_gather", "tfq_grouped_scaled_mm_fp8", "tfq_kv_cache_store",
     "tfq_kv_cache_load", "KV_DTYPE", "tfq_set_autotune", "tfq_autotune_lookup",
@@ -310,6 +310,29 @@ def tfq_quant_linear_fused(x, w_q, w_scale, qtype="fp8", act_qmax: float = 448.0
                                        float(act_qmax), int(scale_block), _ptr(bias), _epi(epi),
                                        _ptr(y), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "tfq_quant_linear_fused")
+    return y
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # TFQ_NOALLOC_WORKSPACE_BYTES of include/tfq.h
+
+
+def tfq_quant_linear_fused_noalloc(x, w_q, w_scale, y, qtype="fp8", act_qmax: float = 448.0,
+                                   scale_block: int = 0, bias=None, epi=None, stream=None):
+    """tfq_quant_linear_fused with the activation codes in the library's own
+    per-GPU device scratch: the C call allocates nothing (the caller passes
+    the output y [m, n] BF16).  Calls that overlap in time on one GPU race."""
+    qt = _qt(qtype)
+    m, k = _arg(x, "x", _BF16, rows=True).shape
+    n = _arg(w_q, "w_q", _CODES, shape=(None, k)).shape[0]
+    blk = int(scale_block)
+    _arg(w_scale, "w_scale", _F32, numel=n if blk == 0 else (-(-n // 128)) * (-(-k // 128)))
+    _opt(bias, "bias", _BF16, numel=n)
+    _arg(y, "y", _BF16, shape=(m, n))
+    _gpu(x=x, w_q=w_q, w_scale=w_scale, bias=bias, y=y)
+    check(lib().tfq_quant_linear_fused_noalloc(_ptr(x), m, k, x.stride(0), _ptr(w_q), _ptr(w_scale),
+                                               n, qt, float(act_qmax), blk, _ptr(bias), _epi(epi),
+                                               _ptr(y), _stream(stream)),
+          "tfq_quant_linear_fused_noalloc")
     return y
 
 

@@ -53,6 +53,8 @@ SIGNATURES = [
     ("tfq_autotune_lookup", _I32, [_I32, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     ("tfq_autotune_clear", None, []),
     ("tfq_autotune_set", _I32, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    ("tfq_quant_linear_fused_noalloc", _I32, [_P, _I64, _I64, _I64, _P, _P, _I64, _I32, _F, _I32,
+                                              _P, _I32, _P, _P]),
     ("tfq_e4m3fn_encode_f32", _I32, [_P, _P, _I64, _P]),
     ("tfq_status_string", ctypes.c_char_p, [_I32]),
     ("tfq_last_hip_error", ctypes.c_int, []),

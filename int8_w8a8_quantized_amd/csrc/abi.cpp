@@ -346,6 +346,49 @@ tfq_status tfq_quant_linear_fused(const void* x_bf16, int64_t m, int64_t k, int6
     return hip_status(tfq::launch_scaled_gemm(g, s));
 }
 
+tfq_status tfq_quant_linear_fused_noalloc(const void* x_bf16, int64_t m, int64_t k, int64_t ld_x,
+                                          const void* w_q, const float* w_scale, int64_t n,
+                                          int32_t qtype, float act_qmax, int32_t scale_block,
+                                          const void* bias_bf16, int32_t epi, void* y_bf16,
+                                          void* stream)
+{
+    static_assert(TFQ_NOALLOC_WORKSPACE_BYTES == tfq::kNoAllocScratchBytes, "one scratch size");
+    if (!x_bf16 || !w_q || !w_scale || !y_bf16) return TFQ_ERR_NULL_POINTER;
+    if (!qtype_ok(qtype) || !epi_ok(epi) || (scale_block != 0 && scale_block != 128) ||
+        (scale_block == 128 && qtype != TFQ_QTYPE_E4M3FN))
+        return TFQ_ERR_UNSUPPORTED;
+    if (m < 1 || m > kMaxDim || k < 16 || k > kMaxDim || k % 16 != 0 || ld_x < k ||
+        ld_x > kMaxDim)
+        return TFQ_ERR_BAD_SHAPE;
+    if (scale_block == 128 && k % 128 != 0) return TFQ_ERR_BAD_SHAPE;
+    const size_t need = workspace_bytes(m, k, scale_block);
+    if (need > tfq::kNoAllocScratchBytes) return TFQ_ERR_WORKSPACE_TOO_SMALL;
+    // host-side checks of the caller's buffers before any HIP call (the
+    // scratch is the library's own: placeholders stand in for it here)
+    const uintptr_t fake = (uintptr_t)1 << 62;  // far from any caller buffer; never used
+    tfq_status st = validate_quantize(x_bf16, m, k, ld_x, qtype, act_qmax, scale_block,
+                                      (void*)fake, (float*)(fake + align256((size_t)(m * k))));
+    if (st != TFQ_OK) return st;
+    st = validate_gemm((void*)fake, (const float*)(fake + align256((size_t)(m * k))), w_q, w_scale, m,
+                       n, k, qtype, scale_block, bias_bf16, epi, y_bf16, nullptr,
+                       qtype == TFQ_QTYPE_INT8 ? 131071 : ((int64_t)1 << 22));
+    if (st != TFQ_OK) return st;
+    if (overlap(range_of(y_bf16, m * n * 2), range_of(x_bf16, ((m - 1) * ld_x + k) * 2)))
+        return TFQ_ERR_ALIAS;
+    if ((st = check_device()) != TFQ_OK) return st;
+    void* ws = nullptr;
+    if ((st = hip_status(tfq::noalloc_scratch(&ws))) != TFQ_OK) return st;
+    uint8_t* codes = (uint8_t*)ws;
+    float* scales = (float*)((uint8_t*)ws + align256((size_t)(m * k)));
+    hipStream_t s = (hipStream_t)stream;
+    st = hip_status(tfq::launch_quantize_rows((const uint16_t*)x_bf16, m, k, ld_x, qtype, act_qmax,
+                                              scale_block, codes, scales, s));
+    if (st != TFQ_OK) return st;
+    tfq::GemmArgs g{codes, (const uint8_t*)w_q, scales, w_scale, (const uint16_t*)bias_bf16,
+                    (uint16_t*)y_bf16, nullptr, m, n, k, qtype, scale_block, epi};
+    return hip_status(tfq::launch_scaled_gemm_with(g, tfq::config_without_tuning(g), s));
+}
+
 tfq_status tfq_quantize_mx(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                            void* q_out, uint32_t* scale_out, void* stream)
 {

@@ -86,6 +86,16 @@ hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t 
 // (tune.cpp), else default_config
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream);
 
+// The allocation-free fused Linear's scratch (noalloc.hip): a file-scope
+// device array of kNoAllocScratchBytes per GPU; noalloc_scratch gives the
+// current device's copy (hipGetSymbolAddress on first use per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** out);
+// the configuration launch_scaled_gemm would use, without ever tuning: the
+// cached one if autotuning is on and the shape has been tuned, else the
+// heuristic (no event creation, no synchronisation)
+GemmConfig config_without_tuning(const GemmArgs& g);
+
 // autotune mode (0 off, 1 on), cache lookup and reset (tune.cpp)
 void set_autotune(int mode);
 int autotune_mode();

@@ -114,6 +114,14 @@ void autotune_clear()
     g_cache.clear();
 }
 
+GemmConfig config_without_tuning(const GemmArgs& g)
+{
+    GemmConfig c = default_config(g);
+    int dev = 0;
+    if (g_mode.load() != 0 && hipGetDevice(&dev) == hipSuccess) (void)find(key_of(dev, g), &c);
+    return c;
+}
+
 hipError_t launch_scaled_gemm(const GemmArgs& g, hipStream_t stream)
 {
     if (g_mode.load() == 0) return launch_scaled_gemm_with(g, default_config(g), stream);

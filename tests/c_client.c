@@ -30,7 +30,8 @@ static const fn_t entry_points[] = {
     (fn_t)tfq_quantize_mxfp6,          (fn_t)tfq_scaled_mm_mxfp6,
     (fn_t)tfq_kv_cache_store,          (fn_t)tfq_kv_cache_load,
     (fn_t)tfq_set_autotune,            (fn_t)tfq_autotune_lookup,
-    (fn_t)tfq_autotune_clear,          (fn_t)tfq_e4m3fn_encode_f32,
+    (fn_t)tfq_autotune_clear,          (fn_t)tfq_autotune_set,
+    (fn_t)tfq_quant_linear_fused_noalloc, (fn_t)tfq_e4m3fn_encode_f32,
     (fn_t)tfq_status_string,           (fn_t)tfq_last_hip_error,
     (fn_t)tfq_abi_version,
 };
@@ -75,6 +76,11 @@ int main(void)
     EXPECT(tfq_quant_linear_fused(p, 16, 128, 128, p + 4096, f, 16, TFQ_QTYPE_E4M3FN, 448.0f, 0, NULL,
                                   TFQ_EPI_NONE, p + 8192, p + 16384, 16, NULL) ==
            TFQ_ERR_WORKSPACE_TOO_SMALL);
+    /* 16384 x 5120 activation codes exceed the 64 MiB device scratch */
+    EXPECT(tfq_quant_linear_fused_noalloc(p, 16384, 5120, 5120, p + 4096, f, 256, TFQ_QTYPE_E4M3FN,
+                                          448.0f, 0, NULL, TFQ_EPI_NONE, p + 8192, NULL) ==
+           TFQ_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(tfq_autotune_set(9, 64, 64, 64, TFQ_EPI_NONE, 0, 0, 4) == TFQ_ERR_UNSUPPORTED);
     EXPECT(tfq_quantize_mx(p, 4, 100, 128, p + 4096, (uint32_t*)(p + 8192), NULL) == TFQ_ERR_BAD_SHAPE);
     EXPECT(tfq_scaled_mm_mxfp8(p, (const uint32_t*)f, p + 8192, (const uint32_t*)f, 16, 16, 100, NULL,
                                TFQ_EPI_NONE, p + 16384, NULL) == TFQ_ERR_BAD_SHAPE);

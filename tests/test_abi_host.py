@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
     from int8_w8a8_quantized_amd._lib import SIGNATURES
@@ -285,3 +285,19 @@ def test_autotune_set_validation(L):
         # a valid candidate: only the missing device stops it
         assert s(1, 4096, 4096, 4096, 0, 0, 1, 4) == DEV
         assert s(0, 4096, 4096, 4096, 1, 0, 0, 8) == DEV
+
+
+@no_gpu_only
+def test_noalloc_fused_validation(L):
+    f = L.tfq_quant_linear_fused_noalloc
+    # (x, m, k, ld_x, w_q, w_scale, n, qtype, act_qmax, scale_block, bias, epi, y, stream)
+    assert f(None, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, None) == NULL
+    assert f(A, 100, 256, 256, B, C, 64, 5, 448.0, 0, None, 0, D, None) == UNSUP
+    assert f(A, 100, 250, 256, B, C, 64, 0, 448.0, 0, None, 0, D, None) == SHAPE
+    assert f(A, 100, 256, 256, B, C, 64, 0, 21.0, 0, None, 0, D, None) == QMAX
+    assert f(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, F + 2, 0, D, None) == ALIGN
+    assert f(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, A + 64, None) == ALIAS
+    # beyond the 64 MiB device scratch: refused before any HIP call
+    assert f(A, 16384, 5120, 5120, B, C, 256, 0, 448.0, 0, None, 0, D, None) == WS
+    # valid: only the missing device stops it
+    assert f(A, 100, 256, 256, B, C, 64, 0, 448.0, 0, None, 0, D, None) == DEV

@@ -27,10 +27,12 @@ def test_host_validation_clean_under_asan_ubsan(tmp_path):
     common = ["-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
               "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     jobs = []
-    for src in ("abi.cpp", "tune.cpp", "quantize.hip", "gemm.hip"):
+    from int8_w8a8_quantized_amd.build import SOURCES
+
+    for src in SOURCES:
         obj = str(tmp_path / (os.path.splitext(src)[0] + ".o"))
         jobs.append(([HIPCC] + common + SAN + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
-    with ThreadPoolExecutor(max_workers=4) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         for r in ex.map(lambda j: subprocess.run(j[0], capture_output=True, text=True), jobs):
             assert r.returncode == 0, r.stderr[-2000:]
     client = str(tmp_path / "c_client.o")
