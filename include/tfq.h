@@ -432,8 +432,9 @@ tfq_status tfq_set_autotune(int32_t mode);
 
 /*
  * The cached configuration of a shape, if any: returns 1 and writes kernel
- * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU) and band (tile rows per
- * band of the tile order), else 0.  kind: 0 FP8 per channel (tfq_scaled_mm_fp8,
+ * (0 = 256x256 tiles, 1 = 256x128 tiles two per CU, 2 = 256x192 tiles; 1
+ * and 2 for per-channel FP8 and INT8 only) and band (tile rows per band of
+ * the tile order), else 0.  kind: 0 FP8 per channel (tfq_scaled_mm_fp8,
  * scale_block 0, and the fused FP8 Linear), 1 INT8, 2 FP8 block-scaled,
  * 3 MXFP8, 4 grouped FP8 (with `groups`), 5 MXFP4, 6 MXFP6 E2M3, 7 MXFP6
  * E3M2.  Looks up the current device's entries.

@@ -218,10 +218,19 @@ struct PipeAcc<kMxE3M2> {
     typedef v16f type;
 };
 
-template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
+// NB: 32-column B fragments per wave, so the tile is 256 x (64 NB): NB = 4
+// (256 columns) for every type, NB = 3 (192 columns) for per-channel FP8 and
+// INT8, whose tile counts can then end on a whole wave of CUs.  Both widths
+// run the same MFMAs over the same K steps for every output, so they give
+// the same bits.
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false, int NB = 4>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_pipe_kernel(const Params p)
 {
+    static_assert(NB == 4 || (NB == 3 && (QT == kE4M3FN || QT == kInt8) && !GROUPED),
+                  "192-column tiles: per-channel FP8 / INT8");
+    constexpr int TBN = 64 * NB;  // tile columns
+    constexpr int WNC = 32 * NB;  // columns per wave
     // MXFP4 rows hold two codes per byte: K counts bytes below, and a stage
     // (128 bytes) holds 256 elements = two 128-element scale groups
     constexpr bool FP4 = QT == kMxE2M1;
@@ -299,9 +308,9 @@ void gemm_pipe_kernel(const Params p)
         map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         m0 = tm * BM;
     }
-    const int n0 = tn * BN;
+    const int n0 = tn * TBN;
     const int K = FP4 ? p.k / 2 : FP6 ? p.k / 4 * 3 : p.k;
-    const int rows_a = min(BM, m_end - m0), rows_b = min(BN, p.n - n0);
+    const int rows_a = min(BM, m_end - m0), rows_b = min(TBN, p.n - n0);
     const v4i ra = buffer_rsrc(p.a + (int64_t)m0 * K, rows_a * K);
     const v4i rb = buffer_rsrc(b_grp + (int64_t)n0 * K, rows_b * K);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -313,13 +322,14 @@ void gemm_pipe_kernel(const Params p)
     // and physical chunk together name 16 different 16-byte bank groups.
     //
     // global -> LDS: each wave moves 8-row groups 8 w + j (j = 0..7) of A
-    // and of B with one 1 KB LDS-DMA load each; every row of a group is one
-    // whole 128-byte line of the operand.  Lane l lands at byte 16 l of the
-    // group -- row l >> 3, physical chunk l & 7 -- so it fetches logical
-    // chunk (l & 7) ^ ((row >> 1) & 7), which is (l & 7) ^ (l >> 4) in even
-    // groups and that ^ 4 in odd ones.
+    // and 2 NB w + j (j < 2 NB) of B with one 1 KB LDS-DMA load each; every
+    // row of a group is one whole 128-byte line of the operand.  Lane l
+    // lands at byte 16 l of the group -- row l >> 3, physical chunk l & 7 --
+    // so it fetches logical chunk (l & 7) ^ ((row >> 1) & 7), which is
+    // (l & 7) ^ (l >> 4) in even groups and that ^ 4 in odd ones.
     const int lc_e = (lane & 7) ^ (lane >> 4), lc_o = lc_e ^ 4;
     const int row_off = (64 * wave + (lane >> 3)) * K;
+    const int b_row_off = (16 * NB * wave + (lane >> 3)) * K;
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
     // LDS -> fragments: for K step ks (0, 1) of a stage, lane reads row
     // (lane & 31), logical chunks 4 ks + 2 h and 4 ks + 2 h + 1 into
@@ -338,15 +348,15 @@ void gemm_pipe_kernel(const Params p)
             rd[ks][e] = fr * PK + ((ch ^ sw) << 4);
         }
     const int a_rd = wm * 128 * PK;
-    const int b_rd = PA + wn * 128 * PK;
+    const int b_rd = PA + wn * WNC * PK;
     const int KT = (K + SK - 1) / SK;
 
     typedef typename PipeAcc<QT>::type acc_t;
-    acc_t acc[4][4];
+    acc_t acc[4][NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
@@ -358,19 +368,29 @@ void gemm_pipe_kernel(const Params p)
         const int k0 = kt * SK;
         const int lc = (j & 1) ? lc_o : lc_e;
         const bool oob = k0 + lc * 16 >= K || (FP6 && lc >= 6);
-        const int off = (row_off + j * 8 * K + k0 + lc * 16) | (int)((unsigned)oob << 31);
-        const uint32_t dst = lds_base + (uint32_t)((kt & 1) * PSTAGE + ab * PA + (8 * wave_u + j) * 1024);
+        const int off = ((ab ? b_row_off : row_off) + j * 8 * K + k0 + lc * 16) | (int)((unsigned)oob << 31);
+        const int grp = ab ? 2 * NB * wave_u + j : 8 * wave_u + j;
+        const uint32_t dst = lds_base + (uint32_t)((kt & 1) * PSTAGE + ab * PA + grp * 1024);
         lds_dma16(ab ? rb : ra, off, dst);
     };
-    // fragments of one K step: B of the 4 column tiles, A of the 4 row tiles
-    struct Frags {
-        v8i b[4], a[4];
+    // the stage's loads in issue order: A and B groups alternating, then the
+    // rest of A (8 + 2 NB loads per wave)
+    constexpr int kLoads = 8 + 2 * NB;
+    auto dma_nth = [&](int kt, int t) {
+        if (t < 4 * NB)
+            dma(kt, t & 1, t >> 1);
+        else
+            dma(kt, 0, t - 2 * NB);
     };
-    // half e of fragment q (B tiles 0..3, then A tiles 0..3) of K step ks
+    // fragments of one K step: B of the NB column tiles, A of the 4 row tiles
+    struct Frags {
+        v8i b[NB], a[4];
+    };
+    // half e of fragment q (B tiles 0..NB-1, then A tiles 0..3) of K step ks
     auto read_part = [&](int buf, int ks, Frags& f, int q, int e) {
-        const uint8_t* s = smem + buf * PSTAGE + (q < 4 ? b_rd + q * 32 * PK : a_rd + (q - 4) * 32 * PK);
+        const uint8_t* s = smem + buf * PSTAGE + (q < NB ? b_rd + q * 32 * PK : a_rd + (q - NB) * 32 * PK);
         const v4i v = *reinterpret_cast<const v4i*>(s + rd[ks][e]);
-        v8i& d = q < 4 ? f.b[q] : f.a[q - 4];
+        v8i& d = q < NB ? f.b[q] : f.a[q - NB];
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
     };
@@ -386,23 +406,27 @@ void gemm_pipe_kernel(const Params p)
             rd6[ks][pc] = fr * PK + (((bo >> 4) ^ sw) << 4) + (bo & 15);
         }
     auto read6 = [&](int buf, int ks, Frags& f, int q, int pc) {
-        const uint8_t* s = smem + buf * PSTAGE + (q < 4 ? b_rd + q * 32 * PK : a_rd + (q - 4) * 32 * PK);
+        const uint8_t* s = smem + buf * PSTAGE + (q < NB ? b_rd + q * 32 * PK : a_rd + (q - NB) * 32 * PK);
         const v2i v = *reinterpret_cast<const v2i*>(s + rd6[ks][pc]);
-        v8i& d = q < 4 ? f.b[q] : f.a[q - 4];
+        v8i& d = q < NB ? f.b[q] : f.a[q - NB];
         d[2 * pc] = v[0];
         d[2 * pc + 1] = v[1];
     };
-    // the fragment reads that go with MFMA i of a K step: one 16-byte half
-    // each (16 per K step), or for MXFP6 one or two 8-byte pieces (24)
+    // the fragment reads that go with MFMA i (of 4 NB) of a K step: the
+    // 2 (NB + 4) 16-byte halves spread evenly (one each for NB = 4), or for
+    // MXFP6 one or two 8-byte pieces (24)
+    constexpr int kMfmas = 4 * NB, kHalves = 2 * (NB + 4);
     auto read_slots = [&](int buf, int ks, Frags& f, int i) {
-        // fragment order A0, B0..B3, A1..A3: the order the next K step's
-        // MFMAs first use them
-        constexpr int ord[8] = {4, 0, 1, 2, 3, 5, 6, 7};
+        // fragment order A0, B0..B(NB-1), A1..A3: the order the next K
+        // step's MFMAs first use them
+        auto ord = [](int k) { return k == 0 ? NB : (k <= NB ? k - 1 : k); };
         if constexpr (FP6) {
 #pragma unroll
-            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, ord[sl / 3], sl % 3);
+            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, ord(sl / 3), sl % 3);
         } else {
-            read_part(buf, ks, f, ord[i >> 1], i & 1);
+#pragma unroll
+            for (int hh = kHalves * i / kMfmas; hh < kHalves * (i + 1) / kMfmas; ++hh)
+                read_part(buf, ks, f, ord(hh >> 1), hh & 1);
         }
     };
     // weights as the first operand: the 32x32 result is the transposed
@@ -526,10 +550,7 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            dma(u, 0, j);
-            dma(u, 1, j);
-        }
+        for (int t = 0; t < kLoads; ++t) dma_nth(u, t);
         if constexpr (MX) dma_mx(u);
     }
     if constexpr (FP4) {
@@ -619,14 +640,14 @@ void gemm_pipe_kernel(const Params p)
             }
         }
     } else {
-        // stage 0 complete: the loads of stage 1 (16, plus 1 scale load for
-        // MXFP8/6) may still be in flight
+        // stage 0 complete: the loads of stage 1 (8 + 2 NB, plus 1 scale load
+        // for MXFP8/6) may still be in flight
         if constexpr (MX)
-            asm volatile("s_waitcnt vmcnt(17)\n\ts_barrier" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kLoads + 1) : "memory");
         else
-            asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kLoads) : "memory");
     #pragma unroll
-        for (int i = 0; i < 16; ++i) read_slots(0, 0, f0, i);
+        for (int i = 0; i < kMfmas; ++i) read_slots(0, 0, f0, i);
         if constexpr (MX) read_mx(0, 0);
 
         for (int kt = 0; kt < KT; kt += 2) {
@@ -634,8 +655,8 @@ void gemm_pipe_kernel(const Params p)
             for (int u = 0; u < 2; ++u) {
                 // K step 0 of stage kt+u from f0; K step 1's fragments into f1
     #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    mfma_one(i >> 2, i & 3, f0, u, 0);
+                for (int i = 0; i < kMfmas; ++i) {
+                    mfma_one(i / NB, i % NB, f0, u, 0);
                     TFQ_FENCE();
                     read_slots(u, 1, f1, i);
                     TFQ_FENCE();
@@ -646,13 +667,15 @@ void gemm_pipe_kernel(const Params p)
                 // the loads of stage kt+u+2
                 if constexpr (MX) read_mx(kt + u + 1, u ^ 1);
     #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    mfma_one(i >> 2, i & 3, f1, u, 1);
+                for (int i = 0; i < kMfmas; ++i) {
+                    mfma_one(i / NB, i % NB, f1, u, 1);
                     TFQ_FENCE();
                     read_slots(u ^ 1, 0, f0, i);
                     if constexpr (MX)
                         if (i == 0) dma_mx(kt + u + 2);
-                    dma(kt + u + 2, i & 1, i >> 1);
+    #pragma unroll
+                    for (int t = kLoads * i / kMfmas; t < kLoads * (i + 1) / kMfmas; ++t)
+                        dma_nth(kt + u + 2, t);
                     TFQ_FENCE();
                 }
             }
@@ -681,10 +704,10 @@ void gemm_pipe_kernel(const Params p)
             const int row = m0 + wm * 128 + mi * 32 + fr;
             if (row >= m_end) continue;
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c0 = n0 + wn * 128 + ni * 32 + 8 * q + 4 * h;
+                    const int c0 = n0 + wn * WNC + ni * 32 + 8 * q + 4 * h;
                     if (c0 < p.n)
                         *reinterpret_cast<v4i*>(p.acc + (int64_t)row * p.n + c0) =
                             v4i{(int)acc[mi][ni][4 * q], (int)acc[mi][ni][4 * q + 1],
@@ -706,12 +729,12 @@ void gemm_pipe_kernel(const Params p)
         // zeros, infinities and NaNs included) unchanged.
         const bool has_bias = bias_grp != nullptr;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+        for (int ni = 0; ni < NB; ++ni) {
             v4f sc[4];
             uint2 braw[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int lc0 = wn * 128 + ni * 32 + 8 * q + 4 * h;
+                const int lc0 = wn * WNC + ni * 32 + 8 * q + 4 * h;
                 if constexpr (!MX) sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
                 braw[q] = *reinterpret_cast<const uint2*>(lds_bias + lc0);
             }
@@ -739,15 +762,17 @@ void gemm_pipe_kernel(const Params p)
                 }
             }
         }
-        // the wave reads back only what it wrote itself
+        // the wave reads back only what it wrote itself: 128 rows of 4 NB
+        // 16-byte chunks (WNC columns)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int ch = lane & 15;
-        const int gcol = n0 + wn * 128 + ch * 8;
+        constexpr int CPR = 4 * NB;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int lrow = j * 4 + (lane >> 4);
+        for (int j = 0; j < 2 * CPR; ++j) {
+            const int idx = j * 64 + lane;
+            const int lrow = idx / CPR, ch = idx - lrow * CPR;
             const v4u d = *reinterpret_cast<const v4u*>(stg + lrow * EPITCH + ch * 16);
             const int grow = m0 + wm * 128 + lrow;
+            const int gcol = n0 + wn * WNC + ch * 8;
             if (grow < m_end && gcol < p.n)
                 *reinterpret_cast<v4u*>(p.y + (int64_t)grow * p.n + gcol) = d;
         }
@@ -1202,13 +1227,23 @@ hipError_t launch_block(Params p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false>
-hipError_t launch_pipe(const Params& p, hipStream_t st)
+template <int QT, int EPI, bool WANT_Y, bool WANT_ACC, bool GROUPED = false, int NB = 4>
+hipError_t launch_pipe(Params p, hipStream_t st)
 {
+    p.tiles_n = (p.n + 64 * NB - 1) / (64 * NB);
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC, GROUPED>), dim3(grid), dim3(256),
-                       0, st, p);
+    hipLaunchKernelGGL((gemm_pipe_kernel<QT, EPI, WANT_Y, WANT_ACC, GROUPED, NB>), dim3(grid),
+                       dim3(256), 0, st, p);
     return hipGetLastError();
+}
+
+// INT8 outputs of the LDS kernel: BF16 and / or raw INT32 sums
+template <int EPI, int NB>
+hipError_t launch_pipe_int8(const Params& p, bool y, bool a, hipStream_t st)
+{
+    if (y && a) return launch_pipe<kInt8, EPI, true, true, false, NB>(p, st);
+    if (y) return launch_pipe<kInt8, EPI, true, false, false, NB>(p, st);
+    return launch_pipe<kInt8, EPI, false, true, false, NB>(p, st);
 }
 
 // Tile rows per band of the tile order (see map_tile).  The 32 tiles in
@@ -1224,19 +1259,49 @@ int band_rows(int64_t m, int64_t n, int64_t k)
     return k >= 8192 ? 2 : 4;
 }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (256 on MI355X).
+int64_t device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus;
+}
+
+// 256- or 192-column tiles for a per-channel FP8 / INT8 grid: the width
+// whose grid ends closer to a whole number of waves over the CUs, the cost
+// taken as waves x tile width (one tile per CU at a time), 256 on a tie.
+// E.g. image-DiT FFN-up 7145 x 12288: 1344 tiles of 256 (5.25 waves) or
+// exactly 1792 of 192 (7 waves); INT8 4096 x 3072: 192 tiles of 256 (0.75
+// of a wave) or exactly 256 of 192.
+bool prefer_192(int64_t m, int64_t n)
+{
+    const int64_t cus = device_cus(), tm = ceil_div(m, BM);
+    return 3 * ceil_div(tm * ceil_div(n, 192), cus) < 4 * ceil_div(tm * ceil_div(n, 256), cus);
+}
+
 }  // namespace
 
-// Heuristic launch configuration: the 256x256 kernel, except for grids of
-// fewer than 64 256x256 tiles, where the 256x128 two-per-CU kernel keeps
-// twice as many CUs busy; band height by K (band_rows).  Measured on MI355X:
-// from 108 tiles up (FP8 and INT8, up to 240 tiles) the 256x256 kernel is
-// 3-38% faster even with CUs idle; at 16 tiles the two-per-CU kernel is
-// slightly ahead.
+// Heuristic launch configuration: the 256x256 kernel, or for per-channel
+// FP8 / INT8 the 256x192 one where its grid fills the last wave better
+// (prefer_192); for grids of fewer than 64 256x256 tiles, the 256x128
+// two-per-CU kernel, which keeps twice as many CUs busy; band height by K
+// (band_rows).  Measured on MI355X: from 108 tiles up (FP8 and INT8, up to
+// 240 tiles) the 256x256 kernel is 3-38% faster than the two-per-CU one
+// even with CUs idle; at 16 tiles the two-per-CU kernel is slightly ahead.
 GemmConfig default_config(const GemmArgs& g)
 {
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
     const bool dual_ok = g.groups == 0 && g.scale_block == 0 && (g.qtype == kE4M3FN || g.qtype == kInt8);
-    return GemmConfig{dual_ok && tiles < 64 ? 1 : 0, band_rows(g.m, g.n, g.k)};
+    const int band = band_rows(g.m, g.n, g.k);
+    if (dual_ok && tiles < 64) return GemmConfig{1, band};
+    if (dual_ok && prefer_192(g.m, g.n)) return GemmConfig{2, band};
+    return GemmConfig{0, band};
 }
 
 int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
@@ -1245,9 +1310,11 @@ int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
     int n = 0;
     const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
     const bool dual_ok = g.groups == 0 && g.scale_block == 0 && (g.qtype == kE4M3FN || g.qtype == kInt8);
-    for (int kernel = 0; kernel < 2; ++kernel) {
+    for (int kernel = 0; kernel < 3; ++kernel) {
         // the two-per-CU kernel only where the grid is small enough to gain
         if (kernel == 1 && !(dual_ok && tiles < 512)) continue;
+        // 192-column tiles: per-channel FP8 and INT8
+        if (kernel == 2 && !dual_ok) continue;
         for (int b : bands)
             if (n < max_out) out[n++] = GemmConfig{kernel, b};
     }
@@ -1321,9 +1388,14 @@ hipError_t launch_scaled_gemm_with(const GemmArgs& g, GemmConfig c, hipStream_t 
         if (dual)
             return g.epi == 1 ? launch_dual<kE4M3FN, 1, true, false>(p, stream)
                               : launch_dual<kE4M3FN, 0, true, false>(p, stream);
+        if (c.kernel == 2)
+            return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false, false, 3>(p, stream)
+                              : launch_pipe<kE4M3FN, 0, true, false, false, 3>(p, stream);
         return g.epi == 1 ? launch_pipe<kE4M3FN, 1, true, false>(p, stream)
                           : launch_pipe<kE4M3FN, 0, true, false>(p, stream);
     }
+    if (c.kernel == 2)
+        return g.epi == 1 ? launch_pipe_int8<1, 3>(p, y, a, stream) : launch_pipe_int8<0, 3>(p, y, a, stream);
     if (dual) {
         if (g.epi == 1) {
             if (y && a) return launch_dual<kInt8, 1, true, true>(p, stream);

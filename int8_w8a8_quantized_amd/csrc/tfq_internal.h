@@ -69,8 +69,8 @@ struct GemmArgs {
 };
 
 // A GEMM launch configuration: kernel 0 = 256x256 tiles, 1 = 256x128 tiles
-// two per CU (per-channel FP8 / INT8 only); band = tile rows per band of the
-// tile order.  Every candidate configuration of a shape gives the same
+// two per CU, 2 = 256x192 tiles (1 and 2: per-channel FP8 / INT8 only); band
+// = tile rows per band of the tile order.  Every candidate configuration of a shape gives the same
 // result bits.
 struct GemmConfig {
     int kernel;

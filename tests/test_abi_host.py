@@ -275,16 +275,19 @@ def test_autotune_set_validation(L):
     s = L.tfq_autotune_set
     assert s(9, 4096, 4096, 4096, 0, 0, 2, 4) == UNSUP       # unknown kind
     assert s(0, 4096, 4096, 4096, 7, 0, 2, 4) == UNSUP       # unknown epilogue
-    assert s(0, 4096, 4096, 4096, 0, 0, 2, 4) == UNSUP       # no such kernel
+    assert s(0, 4096, 4096, 4096, 0, 0, 3, 4) == UNSUP       # no such kernel
     assert s(0, 4096, 4096, 4096, 0, 0, 0, 3) == UNSUP       # band not a candidate
     assert s(0, 4096, 8192, 4096, 0, 0, 1, 4) == UNSUP       # two-per-CU only below 512 tiles
     assert s(2, 4096, 4096, 4096, 0, 0, 1, 4) == UNSUP       # block-scaled: kernel 0 only
+    assert s(3, 4096, 4096, 4096, 0, 0, 2, 4) == UNSUP       # MXFP8: no 192-column tiles
+    assert s(4, 4096, 4096, 4096, 0, 2, 2, 4) == UNSUP       # grouped: no 192-column tiles
     assert s(4, 4096, 4096, 4096, 0, 0, 0, 4) == SHAPE       # grouped needs 1..256 groups
     assert s(0, 0, 4096, 4096, 0, 0, 0, 4) == SHAPE
     if not HAS_GPU_NODE:
         # a valid candidate: only the missing device stops it
         assert s(1, 4096, 4096, 4096, 0, 0, 1, 4) == DEV
         assert s(0, 4096, 4096, 4096, 1, 0, 0, 8) == DEV
+        assert s(0, 4096, 4096, 4096, 0, 0, 2, 2) == DEV
 
 
 @no_gpu_only

@@ -44,7 +44,7 @@ def test_fp8_tuned_equals_default(tfq, M, N, K):
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(y0, y2)
     cfg = tfq.tfq_autotune_lookup("fp8", M, N, K, "gelu_tanh")
-    assert cfg is not None and cfg[0] in (0, 1) and cfg[1] in (1, 2, 4, 8)
+    assert cfg is not None and cfg[0] in (0, 1, 2) and cfg[1] in (1, 2, 4, 8)
     assert tfq.tfq_autotune_lookup("fp8", M, N, K, None) is None   # another key
     # the tuned result against the oracle directly (sampled rows + the ragged tail)
     rows = np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
@@ -56,9 +56,9 @@ def test_fp8_tuned_equals_default(tfq, M, N, K):
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
 def test_every_candidate_configuration(tfq, qtype):
     """tfq_autotune_set pins each candidate configuration of a shape in turn
-    (the 256x256 and the two-per-CU 256x128 kernel, every band height): every
-    one writes the same bits, which match the oracle.  A configuration that
-    is not a candidate is refused."""
+    (256x256 tiles, 256x192 tiles, the two-per-CU 256x128 kernel; every band
+    height): every one writes the same bits, which match the oracle.  A
+    configuration that is not a candidate is refused."""
     M, N, K = 777, 1000, 1040
     rng = np.random.default_rng(17)
     x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
@@ -68,7 +68,7 @@ def test_every_candidate_configuration(tfq, qtype):
     qb, sb = orc.quantize_rows(w, qtype, qmax)
     dt = torch.uint8 if qtype == "fp8" else torch.int8
     a, b, sad, sbd = dev_u8(qa, dt), dev_u8(qb, dt), dev_f32(sa), dev_f32(sb)
-    kernels = (0, 1)
+    kernels = (0, 1, 2)
     epi = "gelu_tanh" if qtype == "fp8" else None  # INT8: the bit-exact BF16 epilogue
     tfq.tfq_set_autotune(1)
     outs = {}
@@ -99,7 +99,7 @@ def test_every_candidate_configuration(tfq, qtype):
     with pytest.raises(tfq.TfqError):
         tfq.tfq_autotune_set(qtype, M, N, K, 5, 4, epi)
     with pytest.raises(tfq.TfqError):
-        tfq.tfq_autotune_set(qtype, M, N, K, 2, 3, epi)
+        tfq.tfq_autotune_set(qtype, M, N, K, 2, 3, epi)   # band 3
 
 
 def test_other_kinds_tuned_equal_default(tfq):

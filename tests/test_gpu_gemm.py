@@ -272,3 +272,42 @@ def test_big_tile_path_and_kernel_choice_invariance(tfq, qtype):
         assert np.array_equal(host_bits(acc)[rows].astype(np.int64), acc_e)
         assert np.array_equal(yb[rows], y_e)
     assert np.array_equal(host_bits(y_small), yb[:256])
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+@pytest.mark.parametrize("M,N,K", [(1300, 968, 1040), (257, 200, 3088)])
+def test_192_column_tiles(tfq, qtype, M, N, K):
+    """The 256x192 tiles pinned through tfq_autotune_set on ragged M, N
+    (N % 192 != 0) and K (K % 128 != 0), with bias and (FP8) GELU: against
+    the oracle, and bit for bit against the 256x256 tiles."""
+    _, _, qa, sa, qb, sb, bias = _operands(M * 7 + N + K, M, N, K, qtype)
+    dt = torch.uint8 if qtype == "fp8" else torch.int8
+    a, b = dev_u8(qa, dt), dev_u8(qb, dt)
+    sad, sbd, bd = dev_f32(sa), dev_f32(sb), dev_bf16(bias)
+    epi = "gelu_tanh" if qtype == "fp8" else None
+    tfq.tfq_set_autotune(1)
+    try:
+        outs = {}
+        for kern in (2, 0):
+            say(f"{qtype} tile width {192 if kern == 2 else 256} M={M} N={N} K={K}")
+            tfq.tfq_autotune_set(qtype, M, N, K, kern, 4, epi)
+            if qtype == "fp8":
+                y = tfq.tfq_scaled_mm_fp8(a, sad, b, sbd, 0, bd, epi)
+                acc = None
+            else:
+                y, acc = tfq.tfq_scaled_mm_int8(a, sad, b, sbd, bd, epi, want_acc=True)
+            torch.cuda.synchronize()
+            outs[kern] = (host_bits(y), None if acc is None else host_bits(acc))
+    finally:
+        tfq.tfq_set_autotune(0)
+        tfq.tfq_autotune_clear()
+    y192, acc192 = outs[2]
+    assert np.array_equal(y192, outs[0][0]), "192- and 256-column tiles differ"
+    if qtype == "fp8":
+        ref = orc.linear_ref_fast(qa, sa, qb, sb, "fp8", bias=bias, gelu=True)
+        assert_fp8_tolerance(y192, ref, f"192-column tiles M={M} N={N} K={K}")
+    else:
+        acc_e, y_e = orc.int8_linear_fast(qa, sa, qb, sb, bias=bias)
+        assert np.array_equal(acc192.astype(np.int64), acc_e)
+        assert np.array_equal(y192, y_e)
+        assert np.array_equal(acc192, outs[0][1])
