@@ -1323,8 +1323,8 @@ int candidate_configs(const GemmArgs& g, GemmConfig* out, int max_out)
 
 bool config_is_candidate(const GemmArgs& g, GemmConfig c)
 {
-    GemmConfig cand[16];
-    const int n = candidate_configs(g, cand, 16);
+    GemmConfig cand[32];
+    const int n = candidate_configs(g, cand, 32);
     for (int i = 0; i < n; ++i)
         if (cand[i].kernel == c.kernel && cand[i].band == c.band) return true;
     return false;

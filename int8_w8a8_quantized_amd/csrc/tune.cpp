@@ -71,8 +71,8 @@ hipError_t time_config(const GemmArgs& g, GemmConfig c, hipStream_t s, hipEvent_
 
 hipError_t tune(const GemmArgs& g, hipStream_t s, GemmConfig* best)
 {
-    GemmConfig cand[16];
-    const int n = candidate_configs(g, cand, 16);
+    GemmConfig cand[32];
+    const int n = candidate_configs(g, cand, 32);
     *best = default_config(g);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     hipError_t err = hipEventCreate(&e0);

@@ -97,7 +97,7 @@ def test_every_candidate_configuration(tfq, qtype):
         assert np.array_equal(first[1][rows].astype(np.int64), acc_e), "INT32 sums differ"
         assert np.array_equal(first[0][rows], y_e), "INT8 BF16 output differs from the oracle"
     with pytest.raises(tfq.TfqError):
-        tfq.tfq_autotune_set(qtype, M, N, K, 5, 4, epi)
+        tfq.tfq_autotune_set(qtype, M, N, K, 7, 4, epi)
     with pytest.raises(tfq.TfqError):
         tfq.tfq_autotune_set(qtype, M, N, K, 2, 3, epi)   # band 3
 
