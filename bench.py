@@ -67,21 +67,26 @@ class EventTimer:
         self.pairs.clear()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    record, or None when the GEMM source has changed since it was taken."""
+def measured_traffic(prefix: str, grid: int, source: str = "gemm.hip"):
+    """HBM bytes per dispatch of the library kernel whose name starts with
+    `prefix` and whose grid has `grid` threads, from the committed rocprofv3
+    counter record, or None when the kernel's source file has changed since
+    it was taken (or the record holds no such kernel)."""
     import hashlib
 
-    rec_path = os.path.join(ROOT, "profiles", "traffic_video_dit_ffn_pair.json")
-    src = os.path.join(ROOT, "int8_w8a8_quantized_amd", "csrc", "gemm.hip")
+    rec_path = os.path.join(ROOT, "profiles", "traffic_kernel_pass.json")
+    src = os.path.join(ROOT, "int8_w8a8_quantized_amd", "csrc", source)
     try:
         rec = json.load(open(rec_path))
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["gemm_source_sha256"]:
+        key = source.split(".")[0] + "_source_sha256"
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec[key]:
             return None
-        r = rec[kernel]
-        return int(r["read_bytes"] + r["write_bytes"])
+        for name, r in rec["kernels"].items():
+            if name.startswith(prefix) and name.endswith(f" grid={grid}"):
+                return int(r["read_bytes"] + r["write_bytes"])
     except (OSError, KeyError, ValueError):
-        return None
+        pass
+    return None
 
 
 def quant_bytes(m, k, group=0):
@@ -500,6 +505,188 @@ def cpu_baseline_per_config(synth, d_c4, g_host):
     return out
 
 
+def kernel_pass(torch, tfq, synth, reps):
+    """Every kernel bench.py times, `reps` launches in a row, on the same
+    seeded inputs and with the heuristic launch configurations: a short
+    program for rocprofv3 counter passes (the full bench runs each workload
+    for minutes under a counter pass).  Order: video-DiT FFN pair (quantise X,
+    up GEMM + GELU, quantise G, down GEMM), image-DiT fused Linear (quantise
+    + GEMM), block-scaled FP8 (1x128-group quantise + GEMM), INT8 (quantise +
+    GEMM)."""
+    tfq.tfq_set_autotune(0)
+    d = synth.make("c4_video_dit")
+    x, w_up, w_dn = (dev_bf16(d[k], torch) for k in ("x", "w", "w_down"))
+    del d
+    wq_up, ws_up = tfq.tfq_quantize_weight_per_channel(w_up, "fp8", 448.0)
+    wq_dn, ws_dn = tfq.tfq_quantize_weight_per_channel(w_dn, "fp8", 448.0)
+    del w_up, w_dn
+    qx, sx = tfq.tfq_quantize_rows(x, "fp8", 448.0)
+    g = tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None, "gelu_tanh")
+    qg, sg = tfq.tfq_quantize_rows(g, "fp8", 448.0)
+    y = tfq.tfq_scaled_mm_fp8(qg, sg, wq_dn, ws_dn)
+    for name, fn in (("c4 quantise X", lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 0, qx, sx)),
+                     ("c4 up GEMM + GELU", lambda: tfq.tfq_scaled_mm_fp8(
+                         qx, sx, wq_up, ws_up, 0, None, "gelu_tanh", g)),
+                     ("c4 quantise G", lambda: tfq.tfq_quantize_rows(g, "fp8", 448.0, 0, qg, sg)),
+                     ("c4 down GEMM", lambda: tfq.tfq_scaled_mm_fp8(qg, sg, wq_dn, ws_dn, 0, None,
+                                                                     None, y))):
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"kernel pass: {name} x{reps}")
+    del x, qx, sx, g, qg, sg, y, wq_up, ws_up, wq_dn, ws_dn
+    torch.cuda.empty_cache()
+    for wl, qt, qmax, blk in (("c3_image_dit", "fp8", 448.0, 0), ("c5_block_fp8", "fp8", 448.0, 128),
+                              ("c2_int8", "int8", 127.0, 0)):
+        d = synth.make(wl)
+        x, w = dev_bf16(d["x"], torch), dev_bf16(d["w"], torch)
+        del d
+        wq, ws = tfq.tfq_quantize_weight_per_channel(w, qt, qmax, blk)
+        for _ in range(reps):
+            if wl == "c3_image_dit":
+                tfq.tfq_quant_linear_fused(x, wq, ws, qt, qmax)
+            else:
+                qa, sa = tfq.tfq_quantize_rows(x, qt, qmax, blk)
+                if qt == "int8":
+                    tfq.tfq_scaled_mm_int8(qa, sa, wq, ws)
+                else:
+                    tfq.tfq_scaled_mm_fp8(qa, sa, wq, ws, blk)
+        torch.cuda.synchronize()
+        log(f"kernel pass: {wl} x{reps}")
+        del x, w, wq, ws
+        torch.cuda.empty_cache()
+
+
+def read_counters(paths, library_only=True):
+    """{kernel key: {counter: [values]}}, {kernel key: {dispatch: seconds}}
+    from rocprofv3 counter_collection.csv files; the key is the demangled
+    name without namespace and argument list, plus the grid size."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = r["Kernel_Name"]
+            if library_only and "tfq::" not in k:
+                continue
+            k = re.sub(r"^void |tfq::\(anonymous namespace\)::|tfq::", "", k)
+            k = re.sub(r"\(.*\)$", "", k).strip()
+            key = f"{k} grid={r['Grid_Size']}"
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            durs[key][(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"])
+                                                   - int(r["Start_Timestamp"])) * 1e-9
+    return vals, durs
+
+
+def traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per dispatch of every library kernel from a FETCH_SIZE and a
+    WRITE_SIZE pass (KiB per dispatch), each scaled by what the same counter
+    reads for a 1 GiB device copy.  Prints the JSON record measured_traffic
+    reads (with the kernel sources' hashes, so a changed kernel reads as
+    unmeasured)."""
+    import hashlib
+
+    def copy_kib(path, counter):
+        vals, _ = read_counters([path], library_only=False)
+        v = [x for k, cs in vals.items() if "copy" in k for x in cs.get(counter, [])]
+        return float(np.median(v))
+
+    f_fac = (1 << 30) / (copy_kib(copy_fetch_csv, "FETCH_SIZE") * 1024)
+    w_fac = (1 << 30) / (copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
+    fv, _ = read_counters([fetch_csv])
+    wv, _ = read_counters([write_csv])
+    kernels = {}
+    for k in sorted(set(fv) & set(wv)):
+        fk, wk = float(np.mean(fv[k]["FETCH_SIZE"])), float(np.mean(wv[k]["WRITE_SIZE"]))
+        kernels[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                      "read_bytes": int(fk * 1024 * f_fac), "write_bytes": int(wk * 1024 * w_fac)}
+    src = os.path.join(ROOT, "int8_w8a8_quantized_amd", "csrc")
+    sha = lambda f: hashlib.sha256(open(os.path.join(src, f), "rb").read()).hexdigest()  # noqa: E731
+    rec = {"note": "HBM bytes per dispatch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (separate "
+                   "runs, KiB per dispatch) scaled by a 1 GiB device copy's readings",
+           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+           "gemm_source_sha256": sha("gemm.hip"), "quantize_source_sha256": sha("quantize.hip"),
+           "kernels": kernels}
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_trace(stats_csv):
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv: the library's
+    kernels one by one, everything else (torch's kernels of the error
+    report and set-up) summed in one line."""
+    import csv
+    import re
+
+    rows, other = [], [0, 0]
+    for r in csv.DictReader(open(stats_csv)):
+        name = r["Name"]
+        if "tfq::" not in name:
+            other[0] += int(r["Calls"])
+            other[1] += int(r["TotalDurationNs"])
+            continue
+        name = re.sub(r"^void |tfq::\(anonymous namespace\)::|tfq::", "", name)
+        name = re.sub(r"\(.*\)$", "", name).strip()
+        rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    print("| kernel | calls | average (us) | min (us) | max (us) | share of kernel time |")
+    print("|---|---|---|---|---|---|")
+    for n, c, a, lo, hi, pc in rows:
+        print(f"| {n} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {pc:.2f}% |")
+    print(f"| (other kernels) | {other[0]} | | | | total {other[1] / 1e6:.1f} ms |")
+
+
+def summarize_counters(paths):
+    """Per-kernel means of rocprofv3 --pmc CSVs (counter_collection.csv of
+    one or more passes), keyed by kernel name and grid size, with derived
+    figures.  MI355X sums these counters over its units, so:
+      clock = GRBM_GUI_ACTIVE / 8 XCDs / duration;
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (SQ_CYCLES / 32 SEs)
+        (the share of shader cycles each SIMD's matrix core is busy);
+      SQ_BUSY_CYCLES / (SQ_CYCLES): the share of cycles the sequencers hold waves;
+      wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES (per wave);
+      LDS bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict
+        cycles per cycle of LDS instruction activity).
+    GRBM_GUI_ACTIVE also counts the GPU's busy time around a dispatch, so
+    the clock figure reads high (even above 2.4 GHz) for kernels of tens of
+    microseconds; it is meaningful for the GEMMs.  Prints a markdown table."""
+    vals, durs = read_counters(paths)
+    rows = []
+    for key, cs in vals.items():
+        m = {c: float(np.mean(v)) for c, v in cs.items()}
+        dur = float(np.mean(list(durs[key].values())))
+        row = {"kernel": key, "dispatches": len(durs[key]), "us": dur * 1e6}
+        if "GRBM_GUI_ACTIVE" in m:
+            row["clock_ghz"] = m["GRBM_GUI_ACTIVE"] / 8 / dur / 1e9
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "SQ_CYCLES" in m:
+            row["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (m["SQ_CYCLES"] / 32)
+        if "SQ_BUSY_CYCLES" in m and "SQ_CYCLES" in m:
+            row["sq_busy"] = m["SQ_BUSY_CYCLES"] / m["SQ_CYCLES"]
+        if "SQ_WAIT_ANY" in m and "SQ_WAVE_CYCLES" in m:
+            row["wait_any_per_wave"] = m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_ACTIVE_INST_LDS" in m:
+            row["lds_conflict_per_lds_active"] = m["SQ_LDS_BANK_CONFLICT"] / max(
+                m["SQ_ACTIVE_INST_LDS"], 1.0)
+        row["raw"] = m
+        rows.append(row)
+    rows.sort(key=lambda r: -r["us"] * r["dispatches"])
+    print("| kernel | dispatches | us | clock GHz | MFMA busy | SQ busy | wait/wave "
+          "| LDS conflict / LDS active |")
+    print("|---|---|---|---|---|---|---|---|")
+    f = lambda r, k, fmt: (fmt % r[k]) if k in r else "-"  # noqa: E731
+    for r in rows:
+        print(f"| {r['kernel']} | {r['dispatches']} | {r['us']:.1f} | {f(r, 'clock_ghz', '%.3f')} "
+              f"| {f(r, 'mfma_busy', '%.3f')} | {f(r, 'sq_busy', '%.3f')} "
+              f"| {f(r, 'wait_any_per_wave', '%.3f')} | {f(r, 'lds_conflict_per_lds_active', '%.4f')} |")
+    print()
+    print("Raw per-dispatch means:")
+    print()
+    for r in rows:
+        print(f"* {r['kernel']}: " + ", ".join(f"{c} {v:.4g}" for c, v in sorted(r["raw"].items())))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -517,7 +704,29 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--kernel-pass", type=int, default=0, metavar="REPS",
+                    help="only launch every timed kernel REPS times in a row (for rocprofv3 "
+                         "counter passes) and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print per-kernel means and derived figures of rocprofv3 --pmc CSVs "
+                         "and exit (no GPU needed)")
+    ap.add_argument("--traffic-record", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM traffic record of rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                         "passes (bench and 1 GiB copy) and exit (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="print the library kernels of a rocprofv3 kernel_stats.csv as a "
+                         "markdown table and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -538,6 +747,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copied 1 GiB three times")
+        return
+    if args.kernel_pass:
+        kernel_pass(torch, tfq, synth, args.kernel_pass)
         return
 
     # per-shape GEMM tuning: the first warm-up step tunes every shape of the step
@@ -598,7 +810,8 @@ def main():
     roofline = {"bound": "mfma", "kernel": "scaled_gemm fp8 (up projection + GELU epilogue)",
                 "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("gemm_up_gelu"),
+                "traffic": measured_traffic("gemm_pipe_kernel<0, 1, true, false, false",
+                                            -(-M // 256) * -(-N // 256) * 256),
                 "algorithmic_bytes": M * K + N * K + 4 * M + 4 * N + 2 * M * N}
     kernels = {
         "quant_x": {"ms": per["quant_x"], "gbs": quant_bytes(M, K) / per["quant_x"] / 1e6},
