@@ -213,6 +213,27 @@ def quality_linear(torch, x, w, y, rows, gelu=False):
     return out
 
 
+def hbm_reference(torch, stream, g):
+    """What plain streaming kernels reach on the quantisers' traffic: torch's
+    BF16 -> E4M3FN cast of G (2 bytes read, 1 written per element: the
+    quantiser's mix without the absmax) and a device copy of G (1:1); median
+    of 20, bytes as moved."""
+    out = {}
+    f8 = torch.empty(g.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    med, _ = time_calls(torch, stream, lambda: f8.copy_(g))
+    out["cast_bf16_to_e4m3fn_2to1"] = {"ms": med, "gbs": 3 * g.numel() / med / 1e6}
+    del f8
+    g2 = torch.empty_like(g)
+    med, _ = time_calls(torch, stream, lambda: g2.copy_(g))
+    out["copy_1to1"] = {"ms": med, "gbs": 4 * g.numel() / med / 1e6}
+    del g2
+    for v in out.values():
+        v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    out["tensor"] = f"G [{g.shape[0]}, {g.shape[1]}] BF16 ({2 * g.numel() / 2**20:.0f} MiB)"
+    torch.cuda.empty_cache()
+    return out
+
+
 def extras(torch, tfq, synth, stream):
     """Secondary workloads, each timed on its own (median of 20 after 5 warmup)."""
     out = {}
@@ -863,6 +884,7 @@ def main():
 
     ext = {}
     if not args.no_extras:
+        ext["hbm_reference"] = hbm_reference(torch, stream, g)
         ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 8)
         torch.cuda.synchronize()
         ext["c4_mxfp6_e2m3_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 6)

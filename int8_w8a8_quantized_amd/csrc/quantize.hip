@@ -14,8 +14,9 @@
 //  * the absmax is taken on the BF16 bit patterns with the sign cleared
 //    (non-negative finite floats order like integers) using packed 16-bit
 //    max, then reduced with DPP row operations and four readlanes;
-//  * x / s is evaluated as q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0)
-//    with r = RN(1/s) (Markstein's correction step).  For 2^-90 <= s <=
+//  * x / s is evaluated as q0 = x*r, e = fma(q0, s, -x), q = fma(-e, r, q0)
+//    with r = RN(1/s) (Markstein's correction step, with the remainder
+//    negated so that a zero x keeps its sign through every step).  For 2^-90 <= s <=
 //    2^126 this equals the correctly rounded quotient whenever |x/s| >=
 //    2^-12, and smaller quotients encode to zero either way (the sign is
 //    restored from x): checked on the host for every BF16 amax and every BF16
@@ -27,6 +28,8 @@
 //    true division.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tfq_internal.h"
 
@@ -68,37 +71,77 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m)
     return max(max(a, b), max(c, d));
 }
 
-// RN(x / s) for the quantiser; see the file comment.
+// RN(x / s) for the quantiser; see the file comment.  How a wave evaluates
+// it: kFast, Markstein's step with no clamp needed; kFastClamp, the same
+// step and the clamp to +-qmax; kDivide, an IEEE division and the clamp.
+enum : int { kFast = 0, kFastClamp = 1, kDivide = 2 };
+
 struct Quotient {
     float s, r;
-    bool fast;
     __device__ __forceinline__ explicit Quotient(float scale)
+        : s(scale), r(scale == 0.0f ? 0.0f : 1.0f / scale)  // correctly rounded reciprocal
     {
-        s = scale;
-        fast = (scale >= 0x1p-90f && scale <= 0x1p126f) || (scale == 0.0f);
-        r = (scale == 0.0f) ? 0.0f : 1.0f / scale;  // correctly rounded reciprocal
     }
-    __device__ __forceinline__ float operator()(float x) const
+    template <int MODE>
+    __device__ __forceinline__ float eval(float x) const
     {
-        float q;
-        if (fast) {
-            float q0 = x * r;
-            float e = __builtin_fmaf(-q0, s, x);
-            q = __builtin_fmaf(e, r, q0);
+        if constexpr (MODE == kDivide) {
+            // a true division keeps the sign of a zero quotient; a lane with
+            // s = 0 (an all-zero row or group in a wave that divides) takes
+            // x * 0 = +-0, as Markstein's step gives it
+            return s != 0.0f ? x / s : x * 0.0f;
         } else {
-            q = x / s;
+            // e = RN(q0 s - x) = -RN(x - q0 s), so q = RN(q0 + RN(x - q0 s) r)
+            // as in the textbook form; every step is odd in x, and for x = -0
+            // (or s = 0, r = 0) the last sum is -0 + -0, so q keeps the sign
+            const float q0 = x * r;
+            const float e = __builtin_fmaf(q0, s, -x);
+            return __builtin_fmaf(-e, r, q0);
         }
-        return __builtin_copysignf(q, x);  // also gives signed zeros for s == 0
+    }
+    // This lane's mode for a row or group with absmax amax.  Inside the
+    // window the quotient is monotone in |x| (correctly rounded for |x/s| >=
+    // 2^-12, below 2^-10 otherwise, and qmax >= 2^-9), so the largest is that
+    // of amax; when it is <= qmax the clamp changes no element.
+    __device__ __forceinline__ int lane_mode(float amax, float qmax) const
+    {
+        if (!((s >= 0x1p-90f && s <= 0x1p126f) || s == 0.0f)) return kDivide;
+        return eval<kFast>(amax) <= qmax ? kFast : kFastClamp;
     }
 };
 
-template <int QT>
+// One mode for the whole wave (a wave-uniform value, so the encode loops
+// branch once): the largest of its lanes' modes.  Every lane gets the same
+// codes as under its own mode: the clamp is exact where it is not needed,
+// and inside the window the division equals Markstein's step wherever
+// |x/s| >= 2^-12, while smaller quotients encode to a signed zero either way.
+__device__ __forceinline__ int wave_mode(int lane_mode)
+{
+    if (__ballot(lane_mode == kDivide)) return kDivide;
+    return __ballot(lane_mode == kFastClamp) ? kFastClamp : kFast;
+}
+
+// f(std::integral_constant<int, MODE>) for the wave's mode
+template <typename F>
+__device__ __forceinline__ void with_mode(int mode, F&& f)
+{
+    if (mode == kFast)
+        f(std::integral_constant<int, kFast>());
+    else if (mode == kFastClamp)
+        f(std::integral_constant<int, kFastClamp>());
+    else
+        f(std::integral_constant<int, kDivide>());
+}
+
+template <int QT, bool CLAMP = true>
 __device__ __forceinline__ uint32_t encode4(float t0, float t1, float t2, float t3, float qmax)
 {
-    t0 = __builtin_amdgcn_fmed3f(t0, -qmax, qmax);
-    t1 = __builtin_amdgcn_fmed3f(t1, -qmax, qmax);
-    t2 = __builtin_amdgcn_fmed3f(t2, -qmax, qmax);
-    t3 = __builtin_amdgcn_fmed3f(t3, -qmax, qmax);
+    if constexpr (CLAMP) {
+        t0 = __builtin_amdgcn_fmed3f(t0, -qmax, qmax);
+        t1 = __builtin_amdgcn_fmed3f(t1, -qmax, qmax);
+        t2 = __builtin_amdgcn_fmed3f(t2, -qmax, qmax);
+        t3 = __builtin_amdgcn_fmed3f(t3, -qmax, qmax);
+    }
     if constexpr (QT == kE4M3FN) {
         // gfx950 converts to OCP E4M3FN with round-to-nearest-even
         int v = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
@@ -117,12 +160,15 @@ __device__ __forceinline__ uint32_t encode4(float t0, float t1, float t2, float 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-template <int QT>
+template <int QT, int MODE>
 __device__ __forceinline__ uint2 encode_chunk(const uint4& v, const Quotient& d, float qmax)
 {
+    constexpr bool C = MODE != kFast;
     uint2 o;
-    o.x = encode4<QT>(d(bf_lo(v.x)), d(bf_hi(v.x)), d(bf_lo(v.y)), d(bf_hi(v.y)), qmax);
-    o.y = encode4<QT>(d(bf_lo(v.z)), d(bf_hi(v.z)), d(bf_lo(v.w)), d(bf_hi(v.w)), qmax);
+    o.x = encode4<QT, C>(d.eval<MODE>(bf_lo(v.x)), d.eval<MODE>(bf_hi(v.x)),
+                         d.eval<MODE>(bf_lo(v.y)), d.eval<MODE>(bf_hi(v.y)), qmax);
+    o.y = encode4<QT, C>(d.eval<MODE>(bf_lo(v.z)), d.eval<MODE>(bf_hi(v.z)),
+                         d.eval<MODE>(bf_lo(v.w)), d.eval<MODE>(bf_hi(v.w)), qmax);
     return o;
 }
 
@@ -186,11 +232,13 @@ __global__ __launch_bounds__(256) void quantize_rows_resident(
     const Quotient d(s);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
     const int nout = (int)(cols >> 3);
+    with_mode(wave_mode(d.lane_mode(amax, qmax)), [&](auto mode) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int idx = c * 64 + lane;
-        if (idx < nout) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
-    }
+        for (int c = 0; c < CH; ++c) {
+            const int idx = c * 64 + lane;
+            if (idx < nout) qr[idx] = encode_chunk<QT, decltype(mode)::value>(v[c], d, qmax);
+        }
+    });
 }
 
 // Long rows resident in registers, WPR waves per row: each wave holds CH
@@ -235,11 +283,13 @@ __global__ __launch_bounds__(256) void quantize_rows_split(
     if (part == 0 && lane == 0) scale[row] = s;
     const Quotient d(s);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
+    with_mode(wave_mode(d.lane_mode(amax, qmax)), [&](auto mode) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int idx = (part * CH + c) * 64 + lane;
-        if (idx < nchunk) qr[idx] = encode_chunk<QT>(v[c], d, qmax);
-    }
+        for (int c = 0; c < CH; ++c) {
+            const int idx = (part * CH + c) * 64 + lane;
+            if (idx < nchunk) qr[idx] = encode_chunk<QT, decltype(mode)::value>(v[c], d, qmax);
+        }
+    });
 }
 
 // Per-row quantisation of long rows: an absmax pass, then a second read.
@@ -264,8 +314,11 @@ __global__ __launch_bounds__(256) void quantize_rows_two_pass(
     if (lane == 0) scale[row] = s;
     const Quotient d(s);
     uint2* qr = reinterpret_cast<uint2*>(q + row * cols);
-    for (int64_t idx = lane; idx < nchunk; idx += 64)
-        qr[idx] = encode_chunk<QT>(ok ? xr[idx] : make_uint4(0u, 0u, 0u, 0u), d, qmax);
+    with_mode(wave_mode(d.lane_mode(amax, qmax)), [&](auto mode) {
+        for (int64_t idx = lane; idx < nchunk; idx += 64)
+            qr[idx] = encode_chunk<QT, decltype(mode)::value>(
+                ok ? xr[idx] : make_uint4(0u, 0u, 0u, 0u), d, qmax);
+    });
 }
 
 // 1x128 groups: 16 lanes x 8 elements cover one group, so every chunk of a
@@ -299,12 +352,16 @@ __global__ __launch_bounds__(256) void quantize_groups128(
             uint32_t m = abs_max_chunk(0u, v[u]);
             m = max(m & 0xFFFFu, m >> 16);
             m = row16_max(m);  // the group's absmax in every lane of the group
-            const float s = __uint_as_float(m << 16) / qmax;
-            if (idx < nchunk) {
-                if ((lane & 15) == 0) sr[idx >> 4] = s;
-                const Quotient d(s);
-                qr[idx] = encode_chunk<QT>(v[u], d, qmax);
-            }
+            const float amax = __uint_as_float(m << 16);
+            const float s = amax / qmax;
+            const Quotient d(s);
+            // (lanes past the row end hold zeros: amax 0, mode kFast)
+            with_mode(wave_mode(d.lane_mode(amax, qmax)), [&](auto mode) {
+                if (idx < nchunk) {
+                    if ((lane & 15) == 0) sr[idx >> 4] = s;
+                    qr[idx] = encode_chunk<QT, decltype(mode)::value>(v[u], d, qmax);
+                }
+            });
         }
     }
 }
@@ -490,12 +547,17 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
         m = max(m & 0xFFFFu, m >> 16);
 #pragma unroll
         for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-        const float s = __uint_as_float(m << 16) / qmax;  // correctly rounded (IEEE division)
+        const float amax = __uint_as_float(m << 16);
+        const float s = amax / qmax;  // correctly rounded (IEEE division)
+        const Quotient d(s);
+        const int mode = wave_mode(d.lane_mode(amax, qmax));
         const int64_t sl = in[u] ? (int64_t)slot[tok[u]] : -1;
         if (lane_on && sl >= 0 && sl < slots) {
             const int64_t row = sl * heads + h[u];
-            const Quotient d(s);
-            reinterpret_cast<uint2*>(cache + row * hd)[li] = encode_chunk<kE4M3FN>(x[u], d, qmax);
+            with_mode(mode, [&](auto md) {
+                reinterpret_cast<uint2*>(cache + row * hd)[li] =
+                    encode_chunk<kE4M3FN, decltype(md)::value>(x[u], d, qmax);
+            });
             if (li == 0) scale[row] = s;
         }
     }
@@ -595,14 +657,18 @@ __global__ __launch_bounds__(256) void quantize_blocks128(
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    const float s = __uint_as_float(m << 16) / qmax;
+    const float amax = __uint_as_float(m << 16);
+    const float s = amax / qmax;
     if (t == 0) scale[nb * kb_count + kb] = s;
     const Quotient d(s);
+    with_mode(wave_mode(d.lane_mode(amax, qmax)), [&](auto mode) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = nb * 128 + r0 + 16 * i;
-        reinterpret_cast<uint2*>(q + row * k + kb * 128)[cc] = encode_chunk<QT>(v[i], d, qmax);
-    }
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = nb * 128 + r0 + 16 * i;
+            reinterpret_cast<uint2*>(q + row * k + kb * 128)[cc] =
+                encode_chunk<QT, decltype(mode)::value>(v[i], d, qmax);
+        }
+    });
 }
 
 __global__ __launch_bounds__(256) void e4m3fn_encode_kernel(const float4* __restrict__ x,
@@ -631,14 +697,23 @@ hipError_t launch_resident(const uint16_t* x, int64_t rows, int64_t cols, int64_
     return hipGetLastError();
 }
 
+// wg_per_cu > 0 caps the workgroups resident on a CU by giving each one an
+// unused share of the CU's 160 KB of LDS.  With two waves per row (rows of
+// 8K-16K columns) two workgroups per CU -- four rows, ~110 KB of loads in
+// flight per CU -- stream best: quantising the video-DiT G [75600, 13824]
+// went from 5.69 to 6.00 TB/s right after the GEMM that writes G, and from
+// 5.41 to 5.90 TB/s on its own (1, 3 or more per CU, or 4 waves per row at
+// 2-6 per CU: 4.7-5.96 TB/s; a persistent double-buffered variant: 5.0-5.5).
 template <int QT, int CH, int WPR>
 hipError_t launch_split(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float qmax,
-                        uint8_t* q, float* s, Src src, hipStream_t st)
+                        uint8_t* q, float* s, Src src, hipStream_t st, int wg_per_cu = 0)
 {
+    constexpr unsigned kLdsPerCu = 160u << 10;
     const int64_t rpb = 4 / WPR;
     const int64_t blocks = (rows + rpb - 1) / rpb;
-    hipLaunchKernelGGL((quantize_rows_split<QT, CH, WPR>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       x, rows, cols, ld, qmax, q, s, src.gather, src.rows);
+    const unsigned pad = wg_per_cu > 0 ? kLdsPerCu / (unsigned)wg_per_cu - 1024u : 0u;
+    hipLaunchKernelGGL((quantize_rows_split<QT, CH, WPR>), dim3((unsigned)blocks), dim3(256), pad,
+                       st, x, rows, cols, ld, qmax, q, s, src.gather, src.rows);
     return hipGetLastError();
 }
 
@@ -655,12 +730,13 @@ hipError_t launch_rows_qt(const uint16_t* x, int64_t rows, int64_t cols, int64_t
     // 4097..6144 columns: 4 waves per row (3% faster at 5120 than one wave;
     // at 3072 one wave per row is 17% faster)
     if (per_lane <= 12) return launch_split<QT, 3, 4>(x, rows, cols, ld, qmax, q, s, src, st);
-    // longer rows: 2 waves per row up to 16384 columns, 4 up to 32768
-    if (per_lane <= 16) return launch_split<QT, 8, 2>(x, rows, cols, ld, qmax, q, s, src, st);
-    if (per_lane <= 20) return launch_split<QT, 10, 2>(x, rows, cols, ld, qmax, q, s, src, st);
-    if (per_lane <= 24) return launch_split<QT, 12, 2>(x, rows, cols, ld, qmax, q, s, src, st);
-    if (per_lane <= 28) return launch_split<QT, 14, 2>(x, rows, cols, ld, qmax, q, s, src, st);
-    if (per_lane <= 32) return launch_split<QT, 16, 2>(x, rows, cols, ld, qmax, q, s, src, st);
+    // longer rows: 2 waves per row up to 16384 columns (two workgroups per
+    // CU, see launch_split), 4 up to 32768
+    if (per_lane <= 16) return launch_split<QT, 8, 2>(x, rows, cols, ld, qmax, q, s, src, st, 2);
+    if (per_lane <= 20) return launch_split<QT, 10, 2>(x, rows, cols, ld, qmax, q, s, src, st, 2);
+    if (per_lane <= 24) return launch_split<QT, 12, 2>(x, rows, cols, ld, qmax, q, s, src, st, 2);
+    if (per_lane <= 28) return launch_split<QT, 14, 2>(x, rows, cols, ld, qmax, q, s, src, st, 2);
+    if (per_lane <= 32) return launch_split<QT, 16, 2>(x, rows, cols, ld, qmax, q, s, src, st, 2);
     if (per_lane <= 48) return launch_split<QT, 12, 4>(x, rows, cols, ld, qmax, q, s, src, st);
     if (per_lane <= 64) return launch_split<QT, 16, 4>(x, rows, cols, ld, qmax, q, s, src, st);
     const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;

@@ -7,8 +7,11 @@
  * for INT8) as one Newton (Markstein) correction of the product with the
  * correctly rounded reciprocal:
  *
- *     r = RN(1 / s);  q0 = RN(x r);  e = RN(x - q0 s) (one fused multiply-add);
- *     q = RN(q0 + e r) (one fused multiply-add)
+ *     r = RN(1 / s);  q0 = RN(x r);  e = RN(q0 s - x) (one fused multiply-add);
+ *     q = RN(q0 - e r) (one fused multiply-add)
+ *
+ * (the remainder is negated against the textbook form so that no step loses
+ * the sign of a zero x; the kernel applies no separate sign fix-up)
  *
  * and use it only for 2^-90 <= s <= 2^126 (or s == 0); other scales take a
  * true division.  This program walks every positive finite BF16 amax, forms
@@ -19,7 +22,9 @@
  *   - below that both must be smaller than 2^-10 in magnitude, so both encode
  *     to a signed zero (E4M3FN's smallest step is 2^-9 and a quotient at or
  *     below half of it rounds to zero; INT8 rounds anything below 1/2 to 0),
- *     and the quantiser takes the sign from x.
+ *     and carry the sign of x (zeros included);
+ *   - no |q| exceeds that of x = amax: the kernel skips the clamp to +-qmax
+ *     for a row whose amax quotient is <= qmax.
  *
  * It also reports, per qmax, how many scales fall outside the fast-path
  * window (those rows divide for real) and checks the window's edges: at the
@@ -53,8 +58,12 @@ static uint32_t u_of(float f)
 static float markstein(float x, float s, float r)
 {
     const float q0 = x * r;
-    const float e = fmaf(-q0, s, x);
-    return fmaf(e, r, q0);
+    /* (the volatile copy keeps the compiler from folding the negation of e
+     * into the first fused multiply-add: -RN(a b - c) and RN(c - a b) differ
+     * in the sign of an exact zero, which is the point of this form) */
+    volatile float ev = fmaf(q0, s, -x);
+    const float e = ev;
+    return fmaf(-e, r, q0);
 }
 
 /* every pair (x, s) with x a BF16 value of magnitude <= amax_bits; returns
@@ -62,6 +71,7 @@ static float markstein(float x, float s, float r)
 static long check_scale(uint32_t amax_bits, float s, long* tested)
 {
     const float r = 1.0f / s;
+    const float top = fabsf(markstein(f_of(amax_bits << 16), s, r));
     long bad = 0;
     for (uint32_t xb = 0; xb <= amax_bits; ++xb) {
         for (int sg = 0; sg < 2; ++sg) {
@@ -71,8 +81,9 @@ static long check_scale(uint32_t amax_bits, float s, long* tested)
             if (fabsf(ref) >= 0x1p-12f) {
                 if (u_of(got) != u_of(ref)) ++bad;
             } else {
-                if (!(fabsf(got) < 0x1p-10f)) ++bad;
+                if (!(fabsf(got) < 0x1p-10f) || signbit(got) != signbit(x)) ++bad;
             }
+            if (fabsf(got) > top) ++bad;
         }
     }
     *tested += 2 * (long)(amax_bits + 1);

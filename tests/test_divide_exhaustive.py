@@ -2,16 +2,18 @@
 
 The row quantisers evaluate x / s (TeleFuser "Quantization", "Scaled FP8
 checkpoints: W8A8" and "Core ideas") as one Markstein correction of x * RN(1/s)
-with fused multiply-adds, and divide for real only when s is outside
+with fused multiply-adds (remainder negated so that zeros keep their sign), and divide for real only when s is outside
 [2^-90, 2^126].  ``divide_check.c`` replays that arithmetic in binary32 on the
 host (FMA and division are correctly rounded there as on the GPU) for every
 positive finite BF16 amax and every BF16 x of either sign with |x| <= amax,
 with s = RN(amax / qmax), and requires:
 
 * the same binary32 quotient as RN(x / s) wherever |x / s| >= 2^-12;
-* below that, a result under 2^-10 in magnitude, which encodes to a signed
-  zero exactly as the true quotient does (E4M3FN rounds anything at or below
-  2^-10 to zero; INT8 anything below 1/2);
+* below that, a result under 2^-10 in magnitude with the sign of x (zeros
+  included), which encodes to the same signed zero as the true quotient
+  (E4M3FN rounds anything at or below 2^-10 to zero; INT8 anything below 1/2);
+* no quotient larger in magnitude than that of x = amax (so a row whose amax
+  quotient is <= qmax needs no clamp);
 * the same at the edges of the fast-path window (s = 2^-90 and s = 2^126).
 
 The qmax values are the ones the workloads use: 448 (E4M3FN), the reduced

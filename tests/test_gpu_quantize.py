@@ -102,6 +102,26 @@ def test_groups_128(tfq, rows, cols):
     _check(tfq, _rows(rows + cols + 3, max(rows, 6), cols), "int8", 127.0, group=128)
 
 
+def test_groups_of_every_kind_in_one_wave(tfq):
+    """The 1x128-group kernel quantises 4 groups of a row per 64-lane chunk,
+    each with its own scale: all-zero groups (s = 0, with -0 elements),
+    subnormal absmax (s below the division shortcut's window), BF16-max
+    groups (s overflows to inf at qmax 0.5) and normal groups side by side."""
+    rng = np.random.default_rng(77)
+    rows, cols = 8, 1024
+    x = synth.to_bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    for r in range(rows):
+        g = np.roll(np.arange(8), r) * 128
+        x[r, g[0]:g[0] + 128] = 0
+        x[r, g[0]:g[0] + 128:3] = 0x8000
+        x[r, g[1]:g[1] + 128] = (np.arange(128) % 5).astype(np.uint16)
+        x[r, g[1]:g[1] + 128:2] |= 0x8000
+        x[r, g[2]:g[2] + 128] = 0x7F7F
+        x[r, g[2] + 1:g[2] + 128:2] = 0xFF7F
+    for qtype, qmax in [("fp8", 448.0), ("fp8", 0.5), ("fp8", 14.0), ("int8", 127.0)]:
+        _check(tfq, x, qtype, qmax, group=128)
+
+
 def test_weight_per_channel_and_blocks(tfq):
     d = synth.make("c5_block_fp8", M=8, K=640, N=384)
     w = d["w"]
