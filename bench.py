@@ -213,6 +213,32 @@ def quality_linear(torch, x, w, y, rows, gelu=False):
     return out
 
 
+def vendor_reference(torch, stream, qx, sx, wq_up, ws_up, qg, sg, wq_dn, ws_dn):
+    """The vendor library's FP8 GEMM on the same codes and scales:
+    torch._scaled_mm (hipBLASLt) with row-wise activation and column-wise
+    weight scales and BF16 output, no bias and no GELU; median of 20 calls
+    for the up and down projections of the step."""
+    out = {"library": "torch._scaled_mm (hipBLASLt), row/column scales, BF16 out, no epilogue"}
+    f8 = torch.float8_e4m3fn
+    for name, a, sa, b, sb in (("up", qx, sx, wq_up, ws_up), ("down", qg, sg, wq_dn, ws_dn)):
+        A, B = a.view(f8), b.view(f8).t()
+        M, K, N = A.shape[0], A.shape[1], B.shape[1]
+
+        def fn():
+            return torch._scaled_mm(A, B, scale_a=sa[:, None], scale_b=sb[None, :],
+                                    out_dtype=torch.bfloat16)
+        try:
+            fn()
+            med, _ = time_calls(torch, stream, fn)
+        except Exception as e:  # noqa: BLE001 -- reported, not fatal
+            out[name] = {"error": str(e)[:200]}
+            continue
+        tf = 2.0 * M * N * K / med / 1e9
+        out[name] = {"ms": med, "tflops": tf, "frac_fp8_peak": tf / FP8_PEAK_TFLOPS}
+        torch.cuda.empty_cache()
+    return out
+
+
 def hbm_reference(torch, stream, g):
     """What plain streaming kernels reach on the quantisers' traffic: torch's
     BF16 -> E4M3FN cast of G (2 bytes read, 1 written per element: the
@@ -884,6 +910,8 @@ def main():
 
     ext = {}
     if not args.no_extras:
+        ext["vendor_reference"] = vendor_reference(torch, stream, qx, sx, wq_up, ws_up, qg, sg,
+                                                   wq_dn, ws_dn)
         ext["hbm_reference"] = hbm_reference(torch, stream, g)
         ext["c4_mxfp8_pair"] = mx_pair(torch, tfq, stream, x, w_up, w_dn, g, y, 8)
         torch.cuda.synchronize()
