@@ -667,6 +667,19 @@ def summarize_trace(stats_csv):
     import csv
     import re
 
+    def short(name):
+        name = re.sub(r"^void |tfq::\(anonymous namespace\)::|tfq::", "", name)
+        return re.sub(r"\(.*\)$", "", name).strip()
+
+    # per-dispatch durations from the kernel trace next to the stats file,
+    # for the median (and the median of the grid's largest dispatches)
+    trace = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    durs = {}
+    if trace != stats_csv and os.path.exists(trace):
+        for r in csv.DictReader(open(trace)):
+            if "tfq::" in r["Kernel_Name"]:
+                durs.setdefault(short(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     rows, other = [], [0, 0]
     for r in csv.DictReader(open(stats_csv)):
         name = r["Name"]
@@ -674,15 +687,15 @@ def summarize_trace(stats_csv):
             other[0] += int(r["Calls"])
             other[1] += int(r["TotalDurationNs"])
             continue
-        name = re.sub(r"^void |tfq::\(anonymous namespace\)::|tfq::", "", name)
-        name = re.sub(r"\(.*\)$", "", name).strip()
-        rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        n = short(name)
+        med = float(np.median(durs[n])) if n in durs else float("nan")
+        rows.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, float(r["MinNs"]) / 1e3,
                      float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    print("| kernel | calls | average (us) | min (us) | max (us) | share of kernel time |")
-    print("|---|---|---|---|---|---|")
-    for n, c, a, lo, hi, pc in rows:
-        print(f"| {n} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {pc:.2f}% |")
-    print(f"| (other kernels) | {other[0]} | | | | total {other[1] / 1e6:.1f} ms |")
+    print("| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of kernel time |")
+    print("|---|---|---|---|---|---|---|")
+    for n, c, a, md, lo, hi, pc in rows:
+        print(f"| {n} | {c} | {a:.1f} | {md:.1f} | {lo:.1f} | {hi:.1f} | {pc:.2f}% |")
+    print(f"| (other kernels) | {other[0]} | | | | | total {other[1] / 1e6:.1f} ms |")
 
 
 def summarize_counters(paths):
