@@ -507,9 +507,9 @@ def cpu_baseline_per_config(synth, d_c4, g_host):
     """The oracle on the host cores for every workload: the quantiser at full
     size (X of each workload, and the video-DiT G), GB/s over the same
     algorithmic bytes as the GPU; the Linear on all rows of the tiny and INT8
-    workloads and on a 32-row sample of the image-DiT and block-scaled ones
+    workloads and on a 256-row sample of the image-DiT and block-scaled ones
     (seconds for the sample and the linear extrapolation to all rows).  About
-    10-15 s on 16 host cores."""
+    10 s on 16 host cores."""
     import oracle as orc
 
     out = {"quantize": {}, "linear": {}}
@@ -528,8 +528,8 @@ def cpu_baseline_per_config(synth, d_c4, g_host):
         tq("c4_video_dit_g", g_host, "fp8", 448.0)
     for wl, qt, qmax, grp, rows in (("c1_tiny_fp8", "fp8", 448.0, 0, None),
                                     ("c2_int8", "int8", 127.0, 0, None),
-                                    ("c3_image_dit", "fp8", 448.0, 0, 32),
-                                    ("c5_block_fp8", "fp8", 448.0, 128, 32)):
+                                    ("c3_image_dit", "fp8", 448.0, 0, 256),
+                                    ("c5_block_fp8", "fp8", 448.0, 128, 256)):
         d = synth.make(wl)
         qa, sa = tq(wl + "_x", d["x"], qt, qmax, grp)
         if grp:
@@ -557,16 +557,15 @@ def kernel_pass(torch, tfq, synth, reps):
     seeded inputs and with the heuristic launch configurations: a short
     program for rocprofv3 counter passes (the full bench runs each workload
     for minutes under a counter pass).  Order: video-DiT FFN pair (quantise X,
-    up GEMM + GELU, quantise G, down GEMM), image-DiT fused Linear (quantise
-    + GEMM), block-scaled FP8 (1x128-group quantise + GEMM), INT8 (quantise +
-    GEMM)."""
+    up GEMM + GELU, quantise G, down GEMM), the same pair's GEMMs in MXFP8,
+    MXFP6 E2M3 and MXFP4, image-DiT fused Linear (quantise + GEMM),
+    block-scaled FP8 (1x128-group quantise + GEMM), INT8 (quantise + GEMM)."""
     tfq.tfq_set_autotune(0)
     d = synth.make("c4_video_dit")
     x, w_up, w_dn = (dev_bf16(d[k], torch) for k in ("x", "w", "w_down"))
     del d
     wq_up, ws_up = tfq.tfq_quantize_weight_per_channel(w_up, "fp8", 448.0)
     wq_dn, ws_dn = tfq.tfq_quantize_weight_per_channel(w_dn, "fp8", 448.0)
-    del w_up, w_dn
     qx, sx = tfq.tfq_quantize_rows(x, "fp8", 448.0)
     g = tfq.tfq_scaled_mm_fp8(qx, sx, wq_up, ws_up, 0, None, "gelu_tanh")
     qg, sg = tfq.tfq_quantize_rows(g, "fp8", 448.0)
@@ -581,7 +580,27 @@ def kernel_pass(torch, tfq, synth, reps):
             fn()
         torch.cuda.synchronize()
         log(f"kernel pass: {name} x{reps}")
-    del x, qx, sx, g, qg, sg, y, wq_up, ws_up, wq_dn, ws_dn
+    del qx, sx, qg, sg, wq_up, ws_up, wq_dn, ws_dn
+    torch.cuda.empty_cache()
+    # the same pair in MXFP8, MXFP6 E2M3 and MXFP4 (GEMMs only)
+    for bits in (8, 6, 4):
+        quant = {8: tfq.tfq_quantize_mx, 4: tfq.tfq_quantize_mxfp4,
+                 6: lambda t: tfq.tfq_quantize_mxfp6(t, "e2m3")}[bits]
+        mm = {8: tfq.tfq_scaled_mm_mxfp8, 4: tfq.tfq_scaled_mm_mxfp4,
+              6: lambda *a: tfq.tfq_scaled_mm_mxfp6(*a[:4], "e2m3", *a[4:])}[bits]
+        qa, sa = quant(x)
+        qu, su = quant(w_up)
+        for _ in range(reps):
+            mm(qa, sa, qu, su, None, "gelu_tanh", g)
+        qg, sg = quant(g)
+        qd, sd = quant(w_dn)
+        for _ in range(reps):
+            mm(qg, sg, qd, sd, None, None, y)
+        torch.cuda.synchronize()
+        log(f"kernel pass: MXFP{bits} up and down GEMMs x{reps}")
+        del qa, sa, qu, su, qg, sg, qd, sd
+        torch.cuda.empty_cache()
+    del x, g, y, w_up, w_dn
     torch.cuda.empty_cache()
     for wl, qt, qmax, blk in (("c3_image_dit", "fp8", 448.0, 0), ("c5_block_fp8", "fp8", 448.0, 128),
                               ("c2_int8", "int8", 127.0, 0)):
