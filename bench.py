@@ -353,8 +353,8 @@ def extras(torch, tfq, synth, stream):
     wq, ws = tfq.tfq_quantize_weight_per_channel(w, "fp8", 448.0)
     y = tfq.tfq_quant_linear_fused(x, wq, ws, "fp8", 448.0)
     qa, sa = tfq.tfq_quantize_rows(x, "fp8", 448.0)
-    # a 128 x 256 quantisation moves 98 KB: its time is the per-call floor
-    # (launch and one row's latency) that the small quantisers above carry
+    # a 128 x 256 quantisation (98 KB): the event-timed cost of a call whose
+    # data movement is negligible, for reading the small quantisers above
     med, _ = time_calls(torch, stream, lambda: tfq.tfq_quantize_rows(x, "fp8", 448.0, 0, qa, sa))
     out["c1_tiny_fp8"] = {"quality": quality_linear(torch, x, w, y, 128),
                           "quantize_x_ms": med}
