@@ -422,7 +422,8 @@ tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int
  * mode 0 (default): every GEMM entry point uses a fixed heuristic
  * configuration.  mode 1: the first call of each (device, kind, m, n, k,
  * epilogue, groups) shape times every candidate configuration (tile order
- * band height; tile shape for small grids) on the caller's buffers and
+ * band height; for per-channel FP8 / INT8 also the tile shape) on the
+ * caller's buffers and
  * stream, caches the fastest and uses it from then on.  That first call
  * waits for the stream; a stream being captured into a graph is never tuned
  * (the cached or the heuristic configuration is used).  Every configuration
