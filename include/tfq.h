@@ -423,11 +423,11 @@ tfq_status tfq_kv_cache_load(const uint8_t* cache, const float* cache_scale, int
  * configuration.  mode 1: the first call of each (device, kind, m, n, k,
  * epilogue, groups) shape times every candidate configuration (tile order
  * band height; for per-channel FP8 / INT8 also the tile shape) on the
- * caller's buffers and
- * stream, caches the fastest and uses it from then on.  That first call
- * waits for the stream; a stream being captured into a graph is never tuned
- * (the cached or the heuristic configuration is used).  Every configuration
- * produces the same result bits.  Other values: TFQ_ERR_UNSUPPORTED.
+ * caller's buffers and stream, caches the fastest and uses it from then on.
+ * That first call waits for the stream; a stream being captured into a
+ * graph is never tuned (the cached or the heuristic configuration is used).
+ * Every configuration produces the same result bits.  Other values:
+ * TFQ_ERR_UNSUPPORTED.
  */
 tfq_status tfq_set_autotune(int32_t mode);
 
