@@ -15,6 +15,12 @@ and per-workload extras (image-DiT FFN-up fused Linear, block-scaled FP8,
 INT8, quantiser GB/s).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu] [--no-clock]
+
+Measurement helpers (no bench line): --kernel-pass REPS launches every timed
+kernel REPS times for rocprofv3 counter passes; --copy-calibration copies
+1 GiB (the FETCH_SIZE / WRITE_SIZE scale); --summarize-trace,
+--summarize-counters and --traffic-record turn rocprofv3 CSVs into the
+tables and the traffic record kept under profiles/.
 """
 from __future__ import annotations
 
