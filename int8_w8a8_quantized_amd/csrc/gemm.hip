@@ -139,6 +139,14 @@ constexpr int PSCL = (PBUF * PSTAGE > 4 * 128 * EPITCH) ? PBUF * PSTAGE : 4 * 12
 constexpr int PMXS = PSCL + 3 * 1024;
 constexpr int PMXRING = 2;
 constexpr int PSMEM = PMXS + PMXRING * 2048;
+// MXFP6: three stages of packed 96-byte rows (A's three 24 KB stages, then
+// B's), then the bias (and the unused scale slots), then a 4-slot ring of
+// E8M0 scale words
+constexpr int P6OP = BM * 96;        // one operand's stage
+constexpr int P6B = 3 * P6OP;        // where B's stages start
+constexpr int P6SCL = 6 * P6OP;
+constexpr int P6MXS = P6SCL + 3 * 1024;
+constexpr int P6SMEM = P6MXS + 4 * 2048;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -235,10 +243,11 @@ void gemm_pipe_kernel(const Params p)
     // (128 bytes) holds 256 elements = two 128-element scale groups
     constexpr bool FP4 = QT == kMxE2M1;
     // MXFP6 rows hold 3 bytes per 4 codes: a stage is 128 elements = 96
-    // bytes, loaded into 128-byte LDS rows whose chunks 6 and 7 stay zero
+    // bytes, kept as packed 96-byte LDS rows (a pipeline of its own below)
     constexpr bool FP6 = QT == kMxE2M3 || QT == kMxE3M2;
     constexpr int SK = FP6 ? 96 : PK;  // K bytes per stage
-    __shared__ __attribute__((aligned(16))) uint8_t smem[FP4 ? PSMEM + 2 * 2048 : PSMEM];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[FP6 ? P6SMEM : FP4 ? PSMEM + 2 * 2048 : PSMEM];
+    constexpr int SCL = FP6 ? P6SCL : PSCL;  // the tile's row / column scales and bias
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -367,7 +376,7 @@ void gemm_pipe_kernel(const Params p)
     auto dma = [&](int kt, int ab, int j) {
         const int k0 = kt * SK;
         const int lc = (j & 1) ? lc_o : lc_e;
-        const bool oob = k0 + lc * 16 >= K || (FP6 && lc >= 6);
+        const bool oob = k0 + lc * 16 >= K;
         const int off = ((ab ? b_row_off : row_off) + j * 8 * K + k0 + lc * 16) | (int)((unsigned)oob << 31);
         const int grp = ab ? 2 * NB * wave_u + j : 8 * wave_u + j;
         const uint32_t dst = lds_base + (uint32_t)((kt & 1) * PSTAGE + ab * PA + grp * 1024);
@@ -394,40 +403,16 @@ void gemm_pipe_kernel(const Params p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[4 * e + i] = v[i];
     };
-    // MXFP6: in K step ks lane half h holds the 24 bytes at row byte
-    // 48 ks + 24 h -- one whole 32-element block, in registers 0-5 -- read as
-    // three 8-byte pieces, each inside one (swizzled) 16-byte chunk
-    int rd6[2][3];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int pc = 0; pc < 3; ++pc) {
-            const int bo = 48 * ks + 24 * h + 8 * pc;
-            rd6[ks][pc] = fr * PK + (((bo >> 4) ^ sw) << 4) + (bo & 15);
-        }
-    auto read6 = [&](int buf, int ks, Frags& f, int q, int pc) {
-        const uint8_t* s = smem + buf * PSTAGE + (q < NB ? b_rd + q * 32 * PK : a_rd + (q - NB) * 32 * PK);
-        const v2i v = *reinterpret_cast<const v2i*>(s + rd6[ks][pc]);
-        v8i& d = q < NB ? f.b[q] : f.a[q - NB];
-        d[2 * pc] = v[0];
-        d[2 * pc + 1] = v[1];
-    };
     // the fragment reads that go with MFMA i (of 4 NB) of a K step: the
-    // 2 (NB + 4) 16-byte halves spread evenly (one each for NB = 4), or for
-    // MXFP6 one or two 8-byte pieces (24)
+    // 2 (NB + 4) 16-byte halves spread evenly (one each for NB = 4)
     constexpr int kMfmas = 4 * NB, kHalves = 2 * (NB + 4);
     auto read_slots = [&](int buf, int ks, Frags& f, int i) {
         // fragment order A0, B0..B(NB-1), A1..A3: the order the next K
         // step's MFMAs first use them
         auto ord = [](int k) { return k == 0 ? NB : (k <= NB ? k - 1 : k); };
-        if constexpr (FP6) {
 #pragma unroll
-            for (int sl = (3 * i) / 2; sl < (3 * (i + 1)) / 2; ++sl) read6(buf, ks, f, ord(sl / 3), sl % 3);
-        } else {
-#pragma unroll
-            for (int hh = kHalves * i / kMfmas; hh < kHalves * (i + 1) / kMfmas; ++hh)
-                read_part(buf, ks, f, ord(hh >> 1), hh & 1);
-        }
+        for (int hh = kHalves * i / kMfmas; hh < kHalves * (i + 1) / kMfmas; ++hh)
+            read_part(buf, ks, f, ord(hh >> 1), hh & 1);
     };
     // weights as the first operand: the 32x32 result is the transposed
     // output tile, so each lane ends up with 4 consecutive columns
@@ -541,17 +526,19 @@ void gemm_pipe_kernel(const Params p)
     // waves 0, 1, 2 fetch the tile's row scales, column scales and bias into
     // LDS (past the end: zeros); issued first, so the prologue's wait covers them
     if (wave_u == 0 && !MX) {
-        lds_dma16(buffer_rsrc(p.sa + m0, rows_a * 4), lane * 16, lds_base + PSCL);
+        lds_dma16(buffer_rsrc(p.sa + m0, rows_a * 4), lane * 16, lds_base + SCL);
     } else if (wave_u == 1 && !MX) {
-        lds_dma16(buffer_rsrc(sb_grp + n0, rows_b * 4), lane * 16, lds_base + PSCL + 1024);
+        lds_dma16(buffer_rsrc(sb_grp + n0, rows_b * 4), lane * 16, lds_base + SCL + 1024);
     } else if (wave_u == 2 && bias_grp != nullptr) {
-        lds_dma16(buffer_rsrc(bias_grp + n0, rows_b * 2), lane * 16, lds_base + PSCL + 2048);
+        lds_dma16(buffer_rsrc(bias_grp + n0, rows_b * 2), lane * 16, lds_base + SCL + 2048);
     }
+    if constexpr (!FP6) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int t = 0; t < kLoads; ++t) dma_nth(u, t);
-        if constexpr (MX) dma_mx(u);
+            for (int t = 0; t < kLoads; ++t) dma_nth(u, t);
+            if constexpr (MX) dma_mx(u);
+        }
     }
     if constexpr (FP4) {
         // MXFP4: a stage is four K steps of 64 elements.  In K step ks lane
@@ -639,9 +626,141 @@ void gemm_pipe_kernel(const Params p)
                 }
             }
         }
+    } else if constexpr (FP6) {
+        // MXFP6: the rows of a stage (128 elements, 96 bytes) lie back to back
+        // in LDS, 24 KB per operand and stage, so three stages fit
+        // and the loads run two stages ahead (stage s + 3 goes out in stage
+        // s's second K step; the barrier of stage s waits for stage s + 1
+        // only).  Load i of wave w moves chunks L = 64 (6 w + i) + lane of an
+        // operand's 1536 16-byte chunks (row L / 6, slot L % 6), landing
+        // contiguously as LDS-DMA writes them.  Row r keeps its six chunks
+        // rotated by (r >> 3) & 3 slots: rows 8 apart start 768 bytes apart
+        // (the same banks), and the rotation spreads the 8-byte fragment
+        // reads of a 32-row tile over the banks.  In K step ks lane half h
+        // reads the 24 bytes at row byte 48 ks + 24 h (one 32-element block)
+        // as three 8-byte pieces into registers 0-5.
+        // per-lane byte offsets of the pieces (wave's rows and the lane's
+        // row, rotated chunk and byte) for A and B; the stage and the 32-row
+        // tile add constants below 64 KB, so every read takes an immediate
+        const int rot6 = (fr >> 3) & 3;
+        int r6a[2][3], r6b[2][3];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc) {
+                const int bo = 48 * ks + 24 * h + 8 * pc;
+                int ph = (bo >> 4) + rot6;
+                ph -= ph >= 6 ? 6 : 0;
+                const int r = fr * 96 + ph * 16 + (bo & 15);
+                r6a[ks][pc] = wm * 128 * 96 + r;
+                r6b[ks][pc] = P6B + wn * WNC * 96 + r;
+            }
+        auto read6p = [&](int buf, int ks, Frags& f, int q, int pc) {
+            const uint8_t* sp = q < NB ? smem + r6b[ks][pc] + buf * P6OP + q * 32 * 96
+                                       : smem + r6a[ks][pc] + buf * P6OP + (q - NB) * 32 * 96;
+            const v2i vv = *reinterpret_cast<const v2i*>(sp);
+            v8i& d = q < NB ? f.b[q] : f.a[q - NB];
+            d[2 * pc] = vv[0];
+            d[2 * pc + 1] = vv[1];
+        };
+        // the 3 (NB + 4) pieces of a K step spread over its MFMAs, in the
+        // order the next K step's MFMAs first use the fragments
+        auto slots6 = [&](int buf, int ks, Frags& f, int i) {
+            auto ord = [](int k) { return k == 0 ? NB : (k <= NB ? k - 1 : k); };
+            constexpr int kPieces = 3 * (NB + 4);
+#pragma unroll
+            for (int sl = kPieces * i / kMfmas; sl < kPieces * (i + 1) / kMfmas; ++sl)
+                read6p(buf, ks, f, ord(sl / 3), sl % 3);
+        };
+        // load i (0..5) of operand ab (0 A, 1 B) of stage kt into buffer
+        // buf; the lane's row and source chunk of each load are fixed
+        int src6[6];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int L = (6 * wave_u + i) * 64 + lane_id_here();
+            const int row = L / 6, c = L - row * 6;
+            int g = c - ((row >> 3) & 3);
+            g += g < 0 ? 6 : 0;
+            src6[i] = row * K + 16 * g;
+        }
+        auto dma6 = [&](int kt, int buf, int ab, int i) {
+            const int k0 = kt * 96;
+            const int off = (src6[i] + k0) | (int)((unsigned)(k0 >= K) << 31);
+            lds_dma16(ab ? rb : ra, off,
+                      lds_base + (uint32_t)(ab * P6B + buf * P6OP + (6 * wave_u + i) * 1024));
+        };
+        constexpr int kLoads6 = 12;  // per wave and stage (plus one scale load)
+        auto dma6_nth = [&](int kt, int buf, int tt) { dma6(kt, buf, tt & 1, tt >> 1); };
+        // E8M0 scale words of stage kt into ring slot kt % 4 (as dma_mx)
+        auto dma_mx6 = [&](int kt) {
+            const int ab = wave_u & 1;
+            const uint32_t dst = lds_base + P6MXS + (kt & 3) * 2048 + ab * 1024;
+            const int off = (kt * (ab ? p.n : p.m) * 4 + lane * 16) | (int)((unsigned)(kt >= KG) << 31);
+            lds_dma16(ab ? reb : rea, off, dst);
+        };
+        auto read_mx6 = [&](int kt, int set) {
+            const uint16_t* sm = reinterpret_cast<const uint16_t*>(smem + P6MXS + (kt & 3) * 2048);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                scA[set][i] = sm[2 * (wm * 128 + i * 32 + fr) + h];
+                scB[set][i] = sm[2 * (256 + wn * 128 + i * 32 + fr) + h];
+            }
+        };
+        // stages 0, 1, 2; then stage 0 complete (stages 1 and 2 may be in flight)
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            dma_mx6(u);
+#pragma unroll
+            for (int tt = 0; tt < kLoads6; ++tt) dma6_nth(u, u, tt);
+        }
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * (kLoads6 + 1)) : "memory");
+#pragma unroll
+        for (int i = 0; i < kMfmas; ++i) slots6(0, 0, f0, i);
+        read_mx6(0, 0);
+        // stage s in buffer BUF = s % 3; the current stage's scales in set 0
+        auto stage6 = [&](int st, auto bufc) {
+            constexpr int BUF = decltype(bufc)::value;
+            constexpr int NBUF = BUF == 2 ? 0 : BUF + 1;
+#pragma unroll
+            for (int i = 0; i < kMfmas; ++i) {
+                mfma_one(i / NB, i % NB, f0, 0, 0);
+                TFQ_FENCE();
+                slots6(BUF, 1, f1, i);
+                TFQ_FENCE();
+            }
+            // stage st + 1 has arrived (stage st + 2's loads may still be in
+            // flight) and every wave has read all of stage st
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kLoads6 + 1)
+                         : "memory");
+            read_mx6(st + 1, 1);
+#pragma unroll
+            for (int i = 0; i < kMfmas; ++i) {
+                mfma_one(i / NB, i % NB, f1, 0, 1);
+                TFQ_FENCE();
+                slots6(NBUF, 0, f0, i);
+                if (i == 0) dma_mx6(st + 3);
+#pragma unroll
+                for (int tt = kLoads6 * i / kMfmas; tt < kLoads6 * (i + 1) / kMfmas; ++tt)
+                    dma6_nth(st + 3, BUF, tt);
+                TFQ_FENCE();
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                scA[0][i] = scA[1][i];
+                scB[0][i] = scB[1][i];
+            }
+        };
+        int st = 0;
+        for (; st + 3 <= KT; st += 3) {
+            stage6(st, std::integral_constant<int, 0>());
+            stage6(st + 1, std::integral_constant<int, 1>());
+            stage6(st + 2, std::integral_constant<int, 2>());
+        }
+        if (st < KT) stage6(st, std::integral_constant<int, 0>());
+        if (st + 1 < KT) stage6(st + 1, std::integral_constant<int, 1>());
     } else {
         // stage 0 complete: the loads of stage 1 (8 + 2 NB, plus 1 scale load
-        // for MXFP8/6) may still be in flight
+        // for MXFP8) may still be in flight
         if constexpr (MX)
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kLoads + 1) : "memory");
         else
@@ -690,9 +809,9 @@ void gemm_pipe_kernel(const Params p)
     // tile mi and column tile ni, output row  wm*128 + mi*32 + fr  and the
     // four consecutive output columns  wn*128 + ni*32 + 8q + 4h + (0..3)  in
     // registers 4q..4q+3 (q = 0..3).
-    const float* lds_sa = reinterpret_cast<const float*>(smem + PSCL);
-    const float* lds_sb = reinterpret_cast<const float*>(smem + PSCL + 1024);
-    const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + PSCL + 2048);
+    const float* lds_sa = reinterpret_cast<const float*>(smem + SCL);
+    const float* lds_sb = reinterpret_cast<const float*>(smem + SCL + 1024);
+    const uint16_t* lds_bias = reinterpret_cast<const uint16_t*>(smem + SCL + 2048);
     // (MXFP8: the sums are already scaled; no row or column scales)
     float srow[4];
 #pragma unroll
