@@ -357,8 +357,12 @@ tfq_status tfq_scaled_mm_mxfp4(const uint8_t* a_q, const uint32_t* a_scale, cons
  * Scale byte = shared + 127 (clamped to [0, 254]); codes = nearest value of
  * x * 2^-shared clamped to the largest, ties to the even code, sign in bit 5
  * (kept for zero).
- *   q_out     [rows, 3 cols / 4] bytes: per row a little-endian bit stream,
- *             element i in bits 6 i .. 6 i + 5; 16-byte aligned.
+ *   q_out     [cols/128, rows, 96] bytes, group-major: the 128 codes of
+ *             group g (elements 128 g .. 128 g + 127) of row r are the 96
+ *             bytes at (g rows + r) 96, a little-endian bit stream with
+ *             element 128 g + i in bits 6 i .. 6 i + 5; 16-byte aligned.
+ *             (A GEMM stage of 128 elements then reads one contiguous panel
+ *             of rows, whole cache lines.)
  *   scale_out [cols/128, rows] scale words as for tfq_quantize_mx.
  *   rows >= 1; cols >= 128, cols % 128 == 0; rows * cols / 32 <= 2^30.
  */
@@ -367,9 +371,9 @@ tfq_status tfq_quantize_mxfp6(const void* x_bf16, int64_t rows, int64_t cols, in
 
 /*
  * MXFP6 GEMM, as tfq_scaled_mm_mxfp8 over 6-bit codes of format fmt (both
- * operands): a_q [m, 3k/4], b_q [n, 3k/4] as tfq_quantize_mxfp6 writes them,
- * a_scale [k/128, m], b_scale [k/128, n] scale words.  TeleFuser
- * "Quantization", converter section (MXFP6 block format).
+ * operands): a_q [k/128, m, 96], b_q [k/128, n, 96] as tfq_quantize_mxfp6
+ * writes them, a_scale [k/128, m], b_scale [k/128, n] scale words.
+ * TeleFuser "Quantization", converter section (MXFP6 block format).
  *   m >= 1; n >= 8, n % 8 == 0; 128 <= k <= 4194304, k % 128 == 0;
  *   m * k / 32 <= 2^30 and n * k / 32 <= 2^30.
  */

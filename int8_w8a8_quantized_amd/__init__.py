@@ -488,16 +488,18 @@ def tfq_scaled_mm_mxfp4(a_q, a_scale, b_q, b_scale, bias=None, epi=None, y=None,
 @_on_stream
 def tfq_quantize_mxfp6(x: torch.Tensor, fmt="e2m3", q_out=None, scale_out=None, stream=None):
     """MXFP6 quantisation of BF16 rows x [rows, cols] (fmt "e2m3" or "e3m2"):
-    returns (codes uint8 [rows, 3 cols / 4], a 6-bit little-endian stream per
-    row; E8M0 scales uint8 [cols/128, rows, 4] as tfq_quantize_mx)."""
+    returns (codes uint8 [cols/128, rows, 96], group-major: q[g, r] holds the
+    128 codes of elements 128 g .. 128 g + 127 of row r as a 6-bit
+    little-endian stream; E8M0 scales uint8 [cols/128, rows, 4] as
+    tfq_quantize_mx)."""
     rows, cols = _arg(x, "x", _BF16, rows=True).shape
     if fmt not in FP6:
         raise ValueError(f"fmt: {fmt!r}, expected one of {list(FP6)}")
     if q_out is None:
-        q_out = torch.empty((rows, cols // 4 * 3), dtype=torch.uint8, device=x.device)
+        q_out = torch.empty((cols // 128, rows, 96), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=x.device)
-    _arg(q_out, "q_out", (torch.uint8,), shape=(rows, cols // 4 * 3))
+    _arg(q_out, "q_out", (torch.uint8,), shape=(cols // 128, rows, 96))
     _mx_scales(scale_out, "scale_out", rows, cols)
     _gpu(x=x, q_out=q_out, scale_out=scale_out)
     check(lib().tfq_quantize_mxfp6(_ptr(x), rows, cols, x.stride(0), FP6[fmt], _ptr(q_out),
@@ -508,22 +510,21 @@ def tfq_quantize_mxfp6(x: torch.Tensor, fmt="e2m3", q_out=None, scale_out=None, 
 @_on_stream
 def tfq_scaled_mm_mxfp6(a_q, a_scale, b_q, b_scale, fmt="e2m3", bias=None, epi=None, y=None,
                         stream=None):
-    """y [m, n] BF16 from MXFP6 operands a_q [m, 3k/4], b_q [n, 3k/4]."""
-    m, kb = _arg(a_q, "a_q", (torch.uint8,), shape=(None, None)).shape
-    n = _arg(b_q, "b_q", (torch.uint8,), shape=(None, kb)).shape[0]
+    """y [m, n] BF16 from MXFP6 operands a_q [k/128, m, 96], b_q [k/128, n,
+    96] as tfq_quantize_mxfp6 writes them."""
+    kg, m, _ = _arg(a_q, "a_q", (torch.uint8,), shape=(None, None, 96)).shape
+    n = _arg(b_q, "b_q", (torch.uint8,), shape=(kg, None, 96)).shape[1]
     if fmt not in FP6:
         raise ValueError(f"fmt: {fmt!r}, expected one of {list(FP6)}")
-    if kb % 3:
-        raise ValueError(f"a_q: {kb} bytes per row is not a whole number of 6-bit codes in 4s")
-    _mx_scales(a_scale, "a_scale", m, kb // 3 * 4)
-    _mx_scales(b_scale, "b_scale", n, kb // 3 * 4)
+    _mx_scales(a_scale, "a_scale", m, kg * 128)
+    _mx_scales(b_scale, "b_scale", n, kg * 128)
     _opt(bias, "bias", _BF16, numel=n)
     if y is None:
         y = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
     _arg(y, "y", _BF16, shape=(m, n))
     _gpu(a_q=a_q, a_scale=a_scale, b_q=b_q, b_scale=b_scale, bias=bias, y=y)
     check(lib().tfq_scaled_mm_mxfp6(_ptr(a_q), _ptr(a_scale), _ptr(b_q), _ptr(b_scale), m, n,
-                                    kb // 3 * 4, FP6[fmt], _ptr(bias), _epi(epi), _ptr(y),
+                                    kg * 128, FP6[fmt], _ptr(bias), _epi(epi), _ptr(y),
                                     _stream(stream)), "tfq_scaled_mm_mxfp6")
     return y
 

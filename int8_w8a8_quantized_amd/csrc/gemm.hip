@@ -631,9 +631,12 @@ void gemm_pipe_kernel(const Params p)
         // in LDS, 24 KB per operand and stage, so three stages fit
         // and the loads run two stages ahead (stage s + 3 goes out in stage
         // s's second K step; the barrier of stage s waits for stage s + 1
-        // only).  Load i of wave w moves chunks L = 64 (6 w + i) + lane of an
-        // operand's 1536 16-byte chunks (row L / 6, slot L % 6), landing
-        // contiguously as LDS-DMA writes them.  Row r keeps its six chunks
+        // only).  The codes are stored group-major, so a stage of the tile's
+        // rows is one contiguous 24 KB panel in memory too: loads read whole
+        // cache lines (row-major 96-byte row pieces straddle 128-byte lines
+        // and cost the loads about 16% more time).  Load i of wave w moves
+        // chunks L = 64 (6 w + i) + lane of an operand's 1536 16-byte chunks
+        // (row L / 6, slot L % 6), landing contiguously as LDS-DMA writes them.  Row r keeps its six chunks
         // rotated by (r >> 3) & 3 slots: rows 8 apart start 768 bytes apart
         // (the same banks), and the rotation spreads the 8-byte fragment
         // reads of a 32-row tile over the banks.  In K step ks lane half h
@@ -681,12 +684,16 @@ void gemm_pipe_kernel(const Params p)
             const int row = L / 6, c = L - row * 6;
             int g = c - ((row >> 3) & 3);
             g += g < 0 ? 6 : 0;
-            src6[i] = row * K + 16 * g;
+            src6[i] = row * 96 + 16 * g;
         }
+        // the tile's rows of stage kt (past the end of K or of the operand's
+        // rows: zeros)
+        auto panel6 = [&](int ab, int kt) {
+            const int64_t first = (int64_t)kt * (ab ? p.n : p.m) + (ab ? n0 : m0);
+            return buffer_rsrc((ab ? p.b : p.a) + first * 96, kt < KT ? (ab ? rows_b : rows_a) * 96 : 0);
+        };
         auto dma6 = [&](int kt, int buf, int ab, int i) {
-            const int k0 = kt * 96;
-            const int off = (src6[i] + k0) | (int)((unsigned)(k0 >= K) << 31);
-            lds_dma16(ab ? rb : ra, off,
+            lds_dma16(panel6(ab, kt), src6[i],
                       lds_base + (uint32_t)(ab * P6B + buf * P6OP + (6 * wave_u + i) * 1024));
         };
         constexpr int kLoads6 = 12;  // per wave and stage (plus one scale load)

@@ -413,8 +413,11 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float inv)
 // with mb mantissa bits and emin = 1 - bias: rint (ties to even) of the
 // exactly scaled value picks the nearest grid point, the even code on a tie,
 // and a carry into the next binade lands on its first code.  Six-bit codes
-// are a little-endian bit stream per row: a lane's 8 codes are 6 bytes, and
-// lane pairs write their 12 bytes as one aligned store.
+// are stored group-major: the 128 codes of group g of row r are a 96-byte
+// little-endian bit stream at byte (g rows + r) 96, so the groups of one K
+// range of all rows lie together (a GEMM stage reads a contiguous panel).  A
+// lane's 8 codes are 6 bytes, and lane pairs write their 12 bytes as one
+// aligned store.
 template <int MB, int EMIN>
 __device__ __forceinline__ uint32_t small_float_code(float v, float vmax)
 {
@@ -482,7 +485,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                 const uint32_t plo = (uint32_t)__shfl_xor((int)lo, 1);
                 const uint32_t phi = (uint32_t)__shfl_xor((int)hi, 1);
                 if (idx < nchunk && (lane & 1) == 0)
-                    *reinterpret_cast<uint3*>(qrow + (int64_t)(idx >> 1) * 12) =
+                    *reinterpret_cast<uint3*>(q + ((int64_t)(idx >> 4) * rows + row) * 96 +
+                                              ((idx >> 1) & 7) * 12) =
                         make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
             }
             if (idx < nchunk) {

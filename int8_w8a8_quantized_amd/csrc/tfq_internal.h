@@ -27,7 +27,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, i
 // MX rows (cols % 128 == 0): E8M0 scale words [cols/128, rows] (bytes 0..3
 // of word (g, r) = blocks 4 g + 0, 2, 1, 3 of row r); elem_bits 8: MXFP8 codes [rows, cols]; 4: MXFP4 codes [rows, cols/2], two
 // per byte (lower index in the low nibble); 62 / 63: MXFP6 E2M3 / E3M2 codes
-// [rows, 3 cols / 4], a little-endian 6-bit stream per row
+// [cols/128, rows, 96]: the 128 codes of group g of row r as a little-endian
+// 6-bit stream at byte (g rows + r) 96
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* q, uint32_t* scale, hipStream_t stream, int elem_bits = 8);
 
@@ -49,8 +50,8 @@ hipError_t launch_quantize_blocks(const uint16_t* w, int64_t n, int64_t k, int q
 hipError_t launch_e4m3fn_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
 
 struct GemmArgs {
-    const uint8_t* a;      // [m, k] codes
-    const uint8_t* b;      // [n, k] codes
+    const uint8_t* a;      // [m, k] codes (MXFP6: [k/128, m, 96])
+    const uint8_t* b;      // [n, k] codes (MXFP6: [k/128, n, 96])
     const float* sa;       // [m] or [m, k/128]
     const float* sb;       // [n] or [n/128, k/128]
     const uint16_t* bias;  // [n] BF16 or null

@@ -75,6 +75,20 @@ def mx_grouped(s):
     return np.ascontiguousarray(s.reshape(r, nb // 4, 4)[:, :, MX_ORDER].transpose(1, 0, 2))
 
 
+def mx6_grouped(q):
+    """MXFP6 codes [rows, 3 cols / 4] (a 6-bit stream per row, as the oracle
+    writes them) -> library layout [cols/128, rows, 96] (96 bytes per
+    128-element group, group-major)."""
+    r, nb = q.shape
+    return np.ascontiguousarray(q.reshape(r, nb // 96, 96).transpose(1, 0, 2))
+
+
+def mx6_ungrouped(q):
+    """Library layout [cols/128, rows, 96] -> MXFP6 codes [rows, 3 cols / 4]."""
+    g, r, _ = q.shape
+    return np.ascontiguousarray(q.transpose(1, 0, 2).reshape(r, 96 * g))
+
+
 def mx_ungrouped(s):
     """Library layout [cols/128, rows, 4] -> oracle scales [rows, cols/32]."""
     g, r, _ = s.shape

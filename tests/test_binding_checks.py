@@ -63,12 +63,14 @@ def test_mx_checks():
     _raises("scale_out", tfq.tfq_quantize_mx, x, scale_out=torch.zeros(2, 8, 3, dtype=torch.uint8))
     _raises("q_out", tfq.tfq_quantize_mxfp4, x, q_out=torch.zeros(8, 256, dtype=torch.uint8))
     _raises("fmt", tfq.tfq_quantize_mxfp6, x, "e5m2")
-    a, b = torch.zeros(8, 192, dtype=torch.uint8), torch.zeros(16, 192, dtype=torch.uint8)
+    a, b = torch.zeros(2, 8, 96, dtype=torch.uint8), torch.zeros(2, 16, 96, dtype=torch.uint8)
     sa, sb = torch.zeros(2, 8, 4, dtype=torch.uint8), torch.zeros(2, 16, 4, dtype=torch.uint8)
+    _raises("q_out", tfq.tfq_quantize_mxfp6, x, q_out=torch.zeros(8, 192, dtype=torch.uint8))
     _raises("a_scale", tfq.tfq_scaled_mm_mxfp6, a, sb, b, sb)
     _raises("fmt", tfq.tfq_scaled_mm_mxfp6, a, sa, b, sb, "e4m3")
-    _raises("a_q", tfq.tfq_scaled_mm_mxfp6, torch.zeros(8, 190, dtype=torch.uint8), sa,
-            torch.zeros(16, 190, dtype=torch.uint8), sb)
+    _raises("a_q", tfq.tfq_scaled_mm_mxfp6, torch.zeros(8, 192, dtype=torch.uint8), sa,
+            torch.zeros(16, 192, dtype=torch.uint8), sb)
+    _raises("b_q", tfq.tfq_scaled_mm_mxfp6, a, sa, torch.zeros(3, 16, 96, dtype=torch.uint8), sb)
     _raises("GPU memory", tfq.tfq_scaled_mm_mxfp6, a, sa, b, sb)
     _raises("b_scale", tfq.tfq_scaled_mm_mxfp8, torch.zeros(8, 256, dtype=torch.uint8), sa,
             torch.zeros(16, 256, dtype=torch.uint8), sa)

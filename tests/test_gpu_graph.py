@@ -75,7 +75,7 @@ def _alloc(tfq):
         "qx8": e((M, K), torch.int8), "sx8": e((M,), f32), "y8": e((M, NU), bf),
         "qxb": e((M, K), u8), "sxb": e((M, K // 128), f32), "yb": e((M, NU), bf),
         "qm8": e((M, K), u8), "sm8": e((K // 128, M, 4), u8), "ym8": e((M, NU), bf),
-        "qm6": e((M, K // 4 * 3), u8), "sm6": e((K // 128, M, 4), u8), "ym6": e((M, NU), bf),
+        "qm6": e((K // 128, M, 96), u8), "sm6": e((K // 128, M, 4), u8), "ym6": e((M, NU), bf),
         "qm4": e((M, K // 2), u8), "sm4": e((K // 128, M, 4), u8), "ym4": e((M, NU), bf),
         "wq": e((NU, K), u8), "wqs": e((NU,), f32),
         "qr": e((R, K), u8), "sr": e((R,), f32), "yr": e((R, NU), bf),

@@ -13,7 +13,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import assert_fp8_tolerance, dev_bf16, host_bits, mx_grouped, needs_gpu, say
+from gpu_util import (assert_fp8_tolerance, dev_bf16, host_bits, mx6_ungrouped, mx_grouped, needs_gpu,
+                      say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -104,10 +105,9 @@ def test_block_scaled_max_k(tfq):
 def test_mx6_max_k(tfq):
     """MXFP6 (E3M2) at the largest K (2^22: 3 MiB code rows)."""
     M, N, K = 512, 264, 1 << 22
-    kb = K // 4 * 3
     g = torch.Generator(device="cuda").manual_seed(4)
-    a = torch.randint(0, 256, (M, kb), dtype=torch.uint8, device="cuda", generator=g)
-    b = torch.randint(0, 256, (N, kb), dtype=torch.uint8, device="cuda", generator=g)
+    a = torch.randint(0, 256, (K // 128, M, 96), dtype=torch.uint8, device="cuda", generator=g)
+    b = torch.randint(0, 256, (K // 128, N, 96), dtype=torch.uint8, device="cuda", generator=g)
     row = _mx_scale_row(K)
     grouped_row = torch.from_numpy(mx_grouped(row[None, :])).cuda()
     sa = grouped_row.expand(K // 128, M, 4).contiguous()
@@ -117,6 +117,7 @@ def test_mx6_max_k(tfq):
     torch.cuda.synchronize()
     cols = np.array([0, 7, 200, N - 1])
     r, c = torch.from_numpy(ROWS), torch.from_numpy(cols)
-    ref = orc.linear_mx6_ref(host_bits(a[r]), np.repeat(row[None, :], ROWS.size, 0), host_bits(b[c]),
+    ref = orc.linear_mx6_ref(mx6_ungrouped(host_bits(a[:, r])), np.repeat(row[None, :], ROWS.size, 0),
+                             mx6_ungrouped(host_bits(b[:, c])),
                              np.repeat(row[None, :], cols.size, 0), "e3m2")
     assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, "mx6 max K")

@@ -1,7 +1,9 @@
 """GPU parity of the MXFP6 path (E2M3 and E3M2 elements) against the oracle.
 
 MXFP6 = 6-bit elements packed as a little-endian bit stream per row, with one
-E8M0 scale per 32 elements along K (TeleFuser "Quantization", converter
+E8M0 scale per 32 elements along K; the library stores each 128-element
+group's 96 bytes group-major ([cols/128, rows, 96]), and these tests move
+the oracle's row streams into that layout and back (a byte permutation) (TeleFuser "Quantization", converter
 section; OCP MX v1.0 block rule, as the oracle states).  Quantisation: packed
 codes and scale bytes bit for bit.  GEMM: BF16 outputs within
 2^-7 |y_ref| + 1e-3 max_row|y_ref| of the oracle's binary64 sum over the
@@ -14,8 +16,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, mx_grouped,
-                      mx_ungrouped, needs_gpu, say)
+from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, mx6_grouped,
+                      mx6_ungrouped, mx_grouped, mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -55,7 +57,7 @@ def test_quantize_mxfp6_bit_exact(tfq, fmt, rows, cols):
     torch.cuda.synchronize()
     qe, se = orc.quantize_mx6(xb, fmt)
     assert np.array_equal(mx_ungrouped(host_bits(s)), se)
-    assert np.array_equal(host_bits(q), qe)
+    assert np.array_equal(mx6_ungrouped(host_bits(q)), qe)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -90,7 +92,7 @@ def test_quantize_mxfp6_special_values_and_stride(tfq, fmt):
     torch.cuda.synchronize()
     qe, se = orc.quantize_mx6(xb[:, :cols], fmt)
     assert np.array_equal(mx_ungrouped(host_bits(s)), se)
-    assert np.array_equal(host_bits(q), qe)
+    assert np.array_equal(mx6_ungrouped(host_bits(q)), qe)
 
 
 def _operands(seed, M, N, K, fmt):
@@ -109,7 +111,7 @@ def _operands(seed, M, N, K, fmt):
                                    (258, 136, 640), (259, 264, 384)])
 def test_mxfp6_gemm(tfq, fmt, M, N, K):
     _, _, qa, sa, qb, sb, bias = _operands(M + 3 * N + K, M, N, K, fmt)
-    a, b = dev_u8(qa), dev_u8(qb)
+    a, b = dev_u8(mx6_grouped(qa)), dev_u8(mx6_grouped(qb))
     sad, sbd = dev_u8(mx_grouped(sa)), dev_u8(mx_grouped(sb))
     for use_bias, epi in [(False, None), (True, None), (True, "gelu_tanh")]:
         say(f"scaled_mm_mxfp6 {fmt} M={M} N={N} K={K} bias={use_bias} epi={epi}")
@@ -136,8 +138,8 @@ def test_mxfp6_single_block_scales(tfq, fmt):
     sa = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
     sb = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
     say(f"scaled_mm_mxfp6 {fmt} single-block M={M} N={N} K={K}")
-    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(qa), dev_u8(mx_grouped(sa)), dev_u8(qb),
-                                dev_u8(mx_grouped(sb)), fmt)
+    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(mx6_grouped(qa)), dev_u8(mx_grouped(sa)),
+                                dev_u8(mx6_grouped(qb)), dev_u8(mx_grouped(sb)), fmt)
     torch.cuda.synchronize()
     ref = orc.linear_mx6_ref(qa, sa, qb, sb, fmt)
     assert_fp8_tolerance(host_bits(y), ref, f"mx6 {fmt} single-block")
@@ -159,8 +161,8 @@ def test_mxfp6_one_hot_codes(tfq, fmt):
     sa = np.full((M, K // 32), 127, np.uint8)
     sb = np.full((N, K // 32), 127, np.uint8)
     say(f"scaled_mm_mxfp6 {fmt} one-hot M={M} N={N} K={K}")
-    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(qa), dev_u8(mx_grouped(sa)), dev_u8(qb),
-                                dev_u8(mx_grouped(sb)), fmt)
+    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(mx6_grouped(qa)), dev_u8(mx_grouped(sa)),
+                                dev_u8(mx6_grouped(qb)), dev_u8(mx_grouped(sb)), fmt)
     torch.cuda.synchronize()
     ref = orc.linear_mx6_ref(qa, sa, qb, sb, fmt)
     # a product of two 6-bit values fits BF16's 8 significant bits exactly
@@ -179,8 +181,10 @@ def test_mxfp6_quantize_then_gemm_end_to_end(tfq, fmt):
     torch.cuda.synchronize()
     qa_e, sa_e = orc.quantize_mx6(xb, fmt)
     qb_e, sb_e = orc.quantize_mx6(wb, fmt)
-    assert np.array_equal(host_bits(qa), qa_e) and np.array_equal(mx_ungrouped(host_bits(sa)), sa_e)
-    assert np.array_equal(host_bits(qb), qb_e) and np.array_equal(mx_ungrouped(host_bits(sb)), sb_e)
+    assert np.array_equal(mx6_ungrouped(host_bits(qa)), qa_e)
+    assert np.array_equal(mx_ungrouped(host_bits(sa)), sa_e)
+    assert np.array_equal(mx6_ungrouped(host_bits(qb)), qb_e)
+    assert np.array_equal(mx_ungrouped(host_bits(sb)), sb_e)
     ref = orc.linear_mx6_ref(qa_e, sa_e, qb_e, sb_e, fmt, bias=bias, gelu=True)
     assert_fp8_tolerance(host_bits(y), ref, f"mx6 {fmt} end-to-end")
 
@@ -190,8 +194,8 @@ def test_mxfp6_big_shape_sampled_rows(tfq, fmt):
     M, N, K = 4100, 4104, 1280
     _, _, qa, sa, qb, sb, _ = _operands(99, M, N, K, fmt)
     say(f"scaled_mm_mxfp6 {fmt} big M={M} N={N} K={K}")
-    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(qa), dev_u8(mx_grouped(sa)), dev_u8(qb),
-                                dev_u8(mx_grouped(sb)), fmt)
+    y = tfq.tfq_scaled_mm_mxfp6(dev_u8(mx6_grouped(qa)), dev_u8(mx_grouped(sa)),
+                                dev_u8(mx6_grouped(qb)), dev_u8(mx_grouped(sb)), fmt)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M)
     rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M),
