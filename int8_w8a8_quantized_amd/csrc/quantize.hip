@@ -415,9 +415,7 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float inv)
 // and a carry into the next binade lands on its first code.  Six-bit codes
 // are stored group-major: the 128 codes of group g of row r are a 96-byte
 // little-endian bit stream at byte (g rows + r) 96, so the groups of one K
-// range of all rows lie together (a GEMM stage reads a contiguous panel).  A
-// lane's 8 codes are 6 bytes, and lane pairs write their 12 bytes as one
-// aligned store.
+// range of all rows lie together (a GEMM stage reads a contiguous panel).
 template <int MB, int EMIN>
 __device__ __forceinline__ uint32_t small_float_code(float v, float vmax)
 {
@@ -435,19 +433,19 @@ __device__ __forceinline__ uint32_t fp6_code(float v)
     return small_float_code<MB, EMIN>(v, VMAX) | ((__float_as_uint(v) >> 26) & 32u);
 }
 
-template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1), 62 / 63: MXFP6 (E2M3 / E3M2)
+template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1)
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
                                                           int64_t rows, int64_t cols, int64_t ld,
                                                           uint8_t* __restrict__ q,
                                                           uint32_t* __restrict__ scale)
 {
     // exponent of the element type's largest normal
-    constexpr int kEmax = F == 8 ? 8 : F == 63 ? 4 : 2;
+    constexpr int kEmax = F == 8 ? 8 : 2;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= rows) return;
     const uint4* xr = reinterpret_cast<const uint4*>(x + row * ld);
-    uint8_t* qrow = q + row * (F == 8 ? cols : F == 4 ? cols / 2 : cols / 4 * 3);
+    uint8_t* qrow = q + row * (F == 8 ? cols : cols / 2);
     const int nchunk = (int)(cols >> 3);  // a multiple of 16: whole groups only
     constexpr int U = 4;
     for (int base = 0; base < nchunk; base += 64 * U) {
@@ -473,27 +471,9 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
                                   ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
-            if constexpr (F == 62 || F == 63) {
-                // 48-bit code group of this lane, then the pair's 12 bytes
-                const uint4 w = v[u];
-                const uint32_t c0 = fp6_code<F>(bf_lo(w.x) * inv), c1 = fp6_code<F>(bf_hi(w.x) * inv),
-                               c2 = fp6_code<F>(bf_lo(w.y) * inv), c3 = fp6_code<F>(bf_hi(w.y) * inv),
-                               c4 = fp6_code<F>(bf_lo(w.z) * inv), c5 = fp6_code<F>(bf_hi(w.z) * inv),
-                               c6 = fp6_code<F>(bf_lo(w.w) * inv), c7 = fp6_code<F>(bf_hi(w.w) * inv);
-                const uint32_t lo = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18) | (c4 << 24) | (c5 << 30);
-                const uint32_t hi = (c5 >> 2) | (c6 << 4) | (c7 << 10);  // 16 bits
-                const uint32_t plo = (uint32_t)__shfl_xor((int)lo, 1);
-                const uint32_t phi = (uint32_t)__shfl_xor((int)hi, 1);
-                if (idx < nchunk && (lane & 1) == 0)
-                    *reinterpret_cast<uint3*>(q + ((int64_t)(idx >> 4) * rows + row) * 96 +
-                                              ((idx >> 1) & 7) * 12) =
-                        make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
-            }
             if (idx < nchunk) {
                 const uint4 w = v[u];
-                if constexpr (F == 62 || F == 63) {
-                    // (stored above)
-                } else if constexpr (F == 8) {
+                if constexpr (F == 8) {
                     uint2 o;
                     o.x = encode4<kE4M3FN>(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv,
                                            bf_hi(w.y) * inv, 448.0f);
@@ -504,6 +484,68 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                     reinterpret_cast<uint32_t*>(qrow)[idx] = e2m1_pack8(w, inv);
                 }
                 if ((lane & 15) == 0) scale[(int64_t)(idx >> 4) * rows + row] = word;
+            }
+        }
+    }
+}
+
+// MXFP6: 16 rows per workgroup, one 128-element group of each at a time.
+// Lane l of wave w takes row 4 w + (l >> 4) of the workgroup and chunk
+// l & 15 (8 elements) of the group, so a 16-lane DPP row is one group of one
+// row, as in quantize_mx_kernel, and the workgroup writes a group's codes
+// for its 16 rows as one contiguous 1536-byte run of the group-major array
+// (one wave per row scattered 96-byte pieces over every group's region:
+// 22% slower on a 75600 x 13824 input).  A lane's 8 codes are 6 bytes, and
+// lane pairs write their 12 bytes as one store.
+template <int F>  // 62: E2M3, 63: E3M2
+__global__ __launch_bounds__(256) void quantize_mx6_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t rows, int64_t cols, int64_t ld,
+                                                           uint8_t* __restrict__ q,
+                                                           uint32_t* __restrict__ scale)
+{
+    constexpr int kEmax = F == 63 ? 4 : 2;
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool live = row < rows;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (live ? row : 0) * ld);
+    const int groups = (int)(cols >> 7);
+    constexpr int U = 4;
+    for (int g0 = 0; g0 < groups; g0 += U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = live && g0 + u < groups ? xr[(g0 + u) * 16 + c] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u;
+            uint32_t m = abs_max_chunk(0u, v[u]);
+            m = max(m & 0xFFFFu, m >> 16);
+            // block max over the 4 lanes of the quad
+            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+            const int code = max((int)((m >> 7) & 0xFFu) - kEmax, 0);
+            const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
+            // the codes of the group's other 3 blocks (lanes +4, +8, +12 of the
+            // 16-lane DPP row) into the group's first lane
+            const uint32_t word = (uint32_t)code |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
+                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
+            const uint4 w = v[u];
+            const uint32_t c0 = fp6_code<F>(bf_lo(w.x) * inv), c1 = fp6_code<F>(bf_hi(w.x) * inv),
+                           c2 = fp6_code<F>(bf_lo(w.y) * inv), c3 = fp6_code<F>(bf_hi(w.y) * inv),
+                           c4 = fp6_code<F>(bf_lo(w.z) * inv), c5 = fp6_code<F>(bf_hi(w.z) * inv),
+                           c6 = fp6_code<F>(bf_lo(w.w) * inv), c7 = fp6_code<F>(bf_hi(w.w) * inv);
+            const uint32_t lo = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18) | (c4 << 24) | (c5 << 30);
+            const uint32_t hi = (c5 >> 2) | (c6 << 4) | (c7 << 10);  // 16 bits
+            const uint32_t plo = (uint32_t)__shfl_xor((int)lo, 1);
+            const uint32_t phi = (uint32_t)__shfl_xor((int)hi, 1);
+            if (live && g < groups) {
+                uint8_t* qg = q + ((int64_t)g * rows + row) * 96;
+                if ((c & 1) == 0)
+                    *reinterpret_cast<uint3*>(qg + (c >> 1) * 12) =
+                        make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
+                if (c == 0) scale[(int64_t)g * rows + row] = word;
             }
         }
     }
@@ -778,8 +820,9 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int
         hipLaunchKernelGGL((quantize_mx_kernel<4>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
                            rows, cols, ld, q, scale);
     else if (elem_bits == 62 || elem_bits == 63)
-        hipLaunchKernelGGL((elem_bits == 62 ? quantize_mx_kernel<62> : quantize_mx_kernel<63>),
-                           dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q, scale);
+        hipLaunchKernelGGL((elem_bits == 62 ? quantize_mx6_kernel<62> : quantize_mx6_kernel<63>),
+                           dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, x, rows, cols, ld,
+                           q, scale);
     else
         hipLaunchKernelGGL((quantize_mx_kernel<8>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
                            rows, cols, ld, q, scale);
