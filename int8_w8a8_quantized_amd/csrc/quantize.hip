@@ -560,8 +560,9 @@ __global__ __launch_bounds__(256) void quantize_mx6_kernel(const uint16_t* __res
 // written to cache row slot[token] * heads + head.  P lanes (a power of two,
 // 8 elements each, P * 8 >= head_dim) hold one vector; a workgroup takes
 // KV_U rounds of 256 / P vectors, all loads first so that KV_U are in
-// flight per lane.  The absmax is combined over the vector's lanes by
-// shuffles.  A slot outside [0, slots) is not written.
+// flight per lane.  The absmax is combined over the vector's lanes by DPP
+// within a 16-lane row (P == 16, head_dim 128: 5% faster than shuffles) or
+// by shuffles.  A slot outside [0, slots) is not written.
 constexpr int KV_U = 4;
 
 template <int P>
@@ -591,8 +592,12 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
     for (int u = 0; u < KV_U; ++u) {
         uint32_t m = abs_max_chunk(0u, x[u]);
         m = max(m & 0xFFFFu, m >> 16);
+        if constexpr (P == 16) {
+            m = row16_max(m);
+        } else {
 #pragma unroll
-        for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+            for (int o = 1; o < P; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        }
         const float amax = __uint_as_float(m << 16);
         const float s = amax / qmax;  // correctly rounded (IEEE division)
         const Quotient d(s);
@@ -613,8 +618,10 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
 // index[i] * heads + head -- the E4M3FN decode is exact, the product is one
 // binary32 multiplication (RNE), then one conversion to the output type
 // (RNE).  An index outside [0, slots) gives a zero vector.  P threads (a
-// power of two, 8 elements each) per vector, KV_U rounds per workgroup with
-// all loads first.
+// power of two, 8 elements each) per vector, KV_LOAD_U rounds per workgroup
+// with all loads first (2 rounds measured 10% faster than 4 at head_dim 128,
+// 8 rounds 20% slower).
+constexpr int KV_LOAD_U = 2;
 typedef float v2f_q __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_q __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h_q __attribute__((ext_vector_type(2)));
@@ -628,12 +635,12 @@ __global__ __launch_bounds__(256) void kv_load_kernel(
     const int nv = (int)(n * heads);
     const int ci = threadIdx.x % P;
     if (ci >= (hd >> 3)) return;
-    int vec[KV_U];
-    uint2 q[KV_U];
-    float s[KV_U];
+    int vec[KV_LOAD_U];
+    uint2 q[KV_LOAD_U];
+    float s[KV_LOAD_U];
 #pragma unroll
-    for (int u = 0; u < KV_U; ++u) {
-        vec[u] = ((int)blockIdx.x * KV_U + u) * (256 / P) + (int)threadIdx.x / P;
+    for (int u = 0; u < KV_LOAD_U; ++u) {
+        vec[u] = ((int)blockIdx.x * KV_LOAD_U + u) * (256 / P) + (int)threadIdx.x / P;
         q[u] = make_uint2(0u, 0u);
         s[u] = 0.0f;
         if (vec[u] < nv) {
@@ -648,7 +655,7 @@ __global__ __launch_bounds__(256) void kv_load_kernel(
         }
     }
 #pragma unroll
-    for (int u = 0; u < KV_U; ++u) {
+    for (int u = 0; u < KV_LOAD_U; ++u) {
         if (vec[u] >= nv) continue;
         // (a zero vector: codes 0 times scale 0)
         v2f_q f[4];
@@ -873,7 +880,7 @@ hipError_t launch_kv_load(const uint8_t* cache, const float* scale, int64_t slot
     const int lanes = (hd + 7) / 8;
     const int64_t nvec = n * heads;
 #define TFQ_KV_LOAD(O, P)                                                                         \
-    hipLaunchKernelGGL((kv_load_kernel<O, P>), dim3((unsigned)((nvec + KV_U * 256 / P - 1) / (KV_U * 256 / P))), \
+    hipLaunchKernelGGL((kv_load_kernel<O, P>), dim3((unsigned)((nvec + KV_LOAD_U * 256 / P - 1) / (KV_LOAD_U * 256 / P))), \
                        dim3(256), 0, stream, cache, scale, slots, heads, hd, index, n, out)
 #define TFQ_KV_LOAD_P(O)       \
     if (lanes <= 4)            \
