@@ -95,6 +95,28 @@ def test_quantize_mxfp6_special_values_and_stride(tfq, fmt):
     assert np.array_equal(mx6_ungrouped(host_bits(q)), qe)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows,cols", [(37, 384), (17, 128)])
+def test_quantize_mxfp6_writes_nothing_past_its_outputs(tfq, fmt, rows, cols):
+    """Codes and scales land in views at the front of larger buffers filled
+    with a sentinel: a workgroup's last rows (rows not a multiple of 16) must
+    not write past either output."""
+    rng = np.random.default_rng(rows + cols)
+    xb = _blocky(rng, rows, cols)
+    nq, ns = cols // 128 * rows * 96, cols // 128 * rows * 4
+    qbuf = torch.full((nq + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((ns + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    q = qbuf[:nq].view(cols // 128, rows, 96)
+    s = sbuf[:ns].view(cols // 128, rows, 4)
+    say(f"quantize_mxfp6 {fmt} guard rows={rows} cols={cols}")
+    tfq.tfq_quantize_mxfp6(dev_bf16(xb), fmt, q, s)
+    torch.cuda.synchronize()
+    assert bool((qbuf[nq:] == 0xA5).all()) and bool((sbuf[ns:] == 0x5A).all())
+    qe, se = orc.quantize_mx6(xb, fmt)
+    assert np.array_equal(mx6_ungrouped(host_bits(q)), qe)
+    assert np.array_equal(mx_ungrouped(host_bits(s)), se)
+
+
 def _operands(seed, M, N, K, fmt):
     rng = np.random.default_rng(seed)
     xb = _blocky(rng, M, K)
