@@ -595,7 +595,10 @@ class QuantLinear:
         w_q, w_s = self.quantized_weight()
         if self.mx:
             quant, mm = self.mx
-            if self._act is None or self._act[0].shape[0] != x.shape[0]:
+            # activation codes and scales are reused while x keeps its shape
+            # (the scales are [cols/128, rows, 4] in every MX format; the
+            # codes' layout differs between formats)
+            if self._act is None or tuple(self._act[1].shape[:2]) != (x.shape[1] // 128, x.shape[0]):
                 self._act = quant(x)
             else:
                 quant(x, *self._act)

@@ -239,14 +239,19 @@ def test_mxfp6_quant_linear_and_tuned_config(tfq, fmt):
     say(f"QuantLinear mxfp6_{fmt} M={M} N={N} K={K}")
     lin = tfq.QuantLinear(dev_bf16(wb), dev_bf16(bias), qtype=f"mxfp6_{fmt}", epi="gelu_tanh")
     y1 = lin(dev_bf16(xb))
-    wq = lin.w_q
+    wq, act = lin.w_q, lin._act[0]
     y2 = lin(dev_bf16(xb))
     qa, sa = tfq.tfq_quantize_mxfp6(dev_bf16(xb), fmt)
     qb, sb = tfq.tfq_quantize_mxfp6(dev_bf16(wb), fmt)
     y3 = tfq.tfq_scaled_mm_mxfp6(qa, sa, qb, sb, fmt, dev_bf16(bias), "gelu_tanh")
     torch.cuda.synchronize()
-    assert lin.w_q is wq
+    assert lin.w_q is wq and lin._act[0] is act   # same shape: buffers reused
     assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    # fewer rows, then the first shape again: new activation buffers, same bits
+    y4 = lin(dev_bf16(xb[:77]))
+    y5 = lin(dev_bf16(xb))
+    torch.cuda.synchronize()
+    assert torch.equal(y4, y1[:77]) and torch.equal(y5, y1)
     say(f"autotune mxfp6_{fmt}")
     tfq.tfq_autotune_clear()
     try:
