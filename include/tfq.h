@@ -51,7 +51,8 @@
 extern "C" {
 #endif
 
-#define TFQ_ABI_VERSION 8
+/* 9: MXFP6 codes are stored group-major, [cols/128, rows, 96] */
+#define TFQ_ABI_VERSION 9
 
 typedef enum tfq_status {
     TFQ_OK = 0,

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.tfq_abi_version() == 8
+    assert L.tfq_abi_version() == 9
     for s in range(10):
         assert L.tfq_status_string(s)
     assert L.tfq_last_hip_error() == 0
