@@ -5,7 +5,8 @@ buffer offset and record count runs at its bound: FP8 on both kernels
 device; outputs are checked on sampled rows x columns against the oracle
 (which takes the matching rows of the operands).  MX scales change with the
 K block (a different power of two every block), so a misplaced scale word
-at a large offset would show.
+at a large offset would show.  MXFP6's group-major codes are also checked
+past 4 GiB of offset.
 """
 import numpy as np
 import pytest
@@ -13,8 +14,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import (assert_fp8_tolerance, dev_bf16, host_bits, mx6_ungrouped, mx_grouped, needs_gpu,
-                      say)
+from gpu_util import (assert_fp8_tolerance, dev_bf16, host_bits, mx6_ungrouped, mx_grouped,
+                      mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -121,3 +122,33 @@ def test_mx6_max_k(tfq):
                              mx6_ungrouped(host_bits(b[:, c])),
                              np.repeat(row[None, :], cols.size, 0), "e3m2")
     assert_fp8_tolerance(host_bits(y)[ROWS][:, cols], ref, "mx6 max K")
+
+
+def test_mx6_group_major_past_4gib(tfq):
+    """MXFP6 codes of a [50000, 131072] input: the group-major array is 4.9 GB,
+    so the last groups' byte offsets ((g rows + r) 96) pass 2^32.  The
+    quantiser's codes and scales for sampled rows (the first, one in the
+    middle, the last) are bit-exact against the oracle, and the GEMM over
+    them (N = 64) is within tolerance on those rows."""
+    M, N, K = 50000, 64, 1 << 17
+    assert (K // 128 - 1) * M * 96 > 1 << 32
+    g = torch.Generator(device="cuda").manual_seed(6)
+    x = torch.randn((M, K), dtype=torch.bfloat16, device="cuda", generator=g)
+    rng = np.random.default_rng(6)
+    wb = synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say(f"mx6 group-major past 4 GiB: M={M} N={N} K={K}")
+    qa, sa = tfq.tfq_quantize_mxfp6(x, "e2m3")
+    qb, sb = tfq.tfq_quantize_mxfp6(dev_bf16(wb), "e2m3")
+    y = tfq.tfq_scaled_mm_mxfp6(qa, sa, qb, sb, "e2m3")
+    torch.cuda.synchronize()
+    rows = np.array([0, 24999, M - 1])
+    r = torch.from_numpy(rows).cuda()
+    xr = host_bits(x[r])
+    del x
+    qe, se = orc.quantize_mx6(xr, "e2m3")
+    assert np.array_equal(mx6_ungrouped(host_bits(qa[:, r])), qe)
+    got_s = host_bits(sa[:, r])
+    assert np.array_equal(mx_ungrouped(got_s), se)
+    qbe, sbe = orc.quantize_mx6(wb, "e2m3")
+    ref = orc.linear_mx6_ref(qe, se, qbe, sbe, "e2m3")
+    assert_fp8_tolerance(host_bits(y[r]), ref, "mx6 past 4 GiB")
