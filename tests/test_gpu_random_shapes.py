@@ -1,6 +1,6 @@
 """Seeded random shapes through the per-channel FP8 and INT8 GEMMs, the
-block-scaled FP8 GEMM, the grouped (routed) FP8 GEMM and the fused Linear,
-against the oracle on every output.
+block-scaled FP8 GEMM, the grouped (routed) FP8 GEMM, the fused Linear and
+the MXFP8 / MXFP4 / MXFP6 quantise + GEMM pairs, against the oracle.
 
 Each case draws M, N and K (ragged against the 256-row, 256- and 192-column
 tiles and the 128-byte K stages) and per-row magnitudes spread over
@@ -23,8 +23,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_f32, dev_u8, host_bits, needs_gpu,
-                      say)
+from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_f32, dev_u8, host_bits, mx6_ungrouped,
+                      mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -78,6 +78,14 @@ OPTIONS = {
     ("block", "small"): (True, G_), ("block", "mid"): (False, None), ("block", "large"): (True, G_),
     ("grouped", "small"): (True, G_), ("grouped", "mid"): (False, None),
     ("fused", "fp8"): (True, G_), ("fused", "int8"): (True, None),
+    ("mxfp8", "small"): (True, None), ("mxfp8", "mid"): (False, G_),
+    ("mxfp4", "small"): (False, G_), ("mxfp4", "mid"): (True, None),
+    ("e2m3", "small"): (True, G_), ("e2m3", "mid"): (False, None),
+    ("e3m2", "small"): (False, None), ("e3m2", "mid"): (True, G_),
+}
+MX_CLASSES = {
+    "small": ((1, 520), (8, 768, 8), (128, 1536, 128)),
+    "mid": ((1800, 2600), (1840, 2640, 8), (128, 768, 128)),
 }
 
 
@@ -199,3 +207,64 @@ def test_fused_strided(tfq, qtype):
     else:
         ref = orc.linear_ref_fast(qa_e, sa_e, qb_e, sb_e, qtype, bias=bias, gelu=epi is not None)
         assert_fp8_tolerance(host_bits(y), ref, f"fused {qtype} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("kind", ["mxfp8", "mxfp4", "e2m3", "e3m2"])
+@pytest.mark.parametrize("cls", list(MX_CLASSES))
+def test_mx(tfq, kind, cls):
+    """MX quantise + GEMM on random shapes, with magnitudes that change by up
+    to 2^+-6 from one 32-element block to the next (a scale applied to the
+    wrong block fails): codes and E8M0 scales bit-exact, then the GEMM on
+    the GPU's codes within the FP8 tolerance (TeleFuser "Quantization",
+    "Offline conversion": 32-value blocks with E8M0 scales).  The mid class
+    is checked on the first and last 8 rows and one row of every 256-row
+    tile."""
+    rng = np.random.default_rng(SEEDS[cls] + 31 + ["mxfp8", "mxfp4", "e2m3", "e3m2"].index(kind))
+    M, N, K = _shape(rng, MX_CLASSES, cls)
+    use_bias, epi = OPTIONS[(kind, cls)]
+
+    def blocky(rows, sigma):
+        x = rng.standard_normal((rows, K)) * sigma
+        x *= np.exp2(rng.integers(-6, 7, (rows, K // 32))).repeat(32, axis=1)
+        return synth.to_bf16_bits(x.astype(np.float32))
+
+    xb, wb = blocky(M, 1.0), blocky(N, 0.02)
+    bb = synth.to_bf16_bits((rng.standard_normal(N) * 0.5).astype(np.float32))
+    say(f"random {kind} {cls} M={M} N={N} K={K} bias={use_bias} epi={epi}")
+    bd, bias, gelu = (dev_bf16(bb) if use_bias else None), (bb if use_bias else None), epi is not None
+    if kind == "mxfp8":
+        qa, sa = tfq.tfq_quantize_mx(dev_bf16(xb))
+        qb, sb = tfq.tfq_quantize_mx(dev_bf16(wb))
+        y = tfq.tfq_scaled_mm_mxfp8(qa, sa, qb, sb, bd, epi)
+        (qa_e, sa_e), (qb_e, sb_e) = orc.quantize_mx(xb), orc.quantize_mx(wb)
+        codes = host_bits
+    elif kind == "mxfp4":
+        qa, sa = tfq.tfq_quantize_mxfp4(dev_bf16(xb))
+        qb, sb = tfq.tfq_quantize_mxfp4(dev_bf16(wb))
+        y = tfq.tfq_scaled_mm_mxfp4(qa, sa, qb, sb, bd, epi)
+        (qa_e, sa_e), (qb_e, sb_e) = orc.quantize_mx4(xb), orc.quantize_mx4(wb)
+        codes = host_bits
+    else:
+        qa, sa = tfq.tfq_quantize_mxfp6(dev_bf16(xb), kind)
+        qb, sb = tfq.tfq_quantize_mxfp6(dev_bf16(wb), kind)
+        y = tfq.tfq_scaled_mm_mxfp6(qa, sa, qb, sb, kind, bd, epi)
+        (qa_e, sa_e), (qb_e, sb_e) = orc.quantize_mx6(xb, kind), orc.quantize_mx6(wb, kind)
+
+        def codes(t):
+            return mx6_ungrouped(host_bits(t))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(qa), qa_e) and np.array_equal(mx_ungrouped(host_bits(sa)), sa_e)
+    assert np.array_equal(codes(qb), qb_e) and np.array_equal(mx_ungrouped(host_bits(sb)), sb_e)
+    rows = None
+    if cls != "small":
+        rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M),
+                                         np.arange(0, M, 256) + rng.integers(0, 256, (M + 255) // 256)]))
+        rows = rows[rows < M]
+    if kind == "mxfp8":
+        ref = orc.linear_mx_ref(qa_e, sa_e, qb_e, sb_e, bias=bias, gelu=gelu, rows=rows)
+    elif kind == "mxfp4":
+        ref = orc.linear_mx4_ref(qa_e, sa_e, qb_e, sb_e, bias=bias, gelu=gelu, rows=rows)
+    else:
+        ref = orc.linear_mx6_ref(qa_e, sa_e, qb_e, sb_e, kind, bias=bias, gelu=gelu, rows=rows)
+    yb = host_bits(y)
+    assert_fp8_tolerance(yb if rows is None else yb[rows], ref, f"{kind} {cls} M={M} N={N} K={K}")
