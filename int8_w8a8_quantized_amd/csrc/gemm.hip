@@ -850,44 +850,53 @@ void gemm_pipe_kernel(const Params p)
         // The column scales and bias values of a column tile are read from LDS
         // together, with one wait, so that the arithmetic is not broken up by
         // waits (LDS operations complete in order: a wait for a read also
-        // waits for the staging writes issued before it).  Bias is always
-        // added: without one it is -0.0, which leaves every value (signed
-        // zeros, infinities and NaNs included) unchanged.
-        const bool has_bias = bias_grp != nullptr;
+        // waits for the staging writes issued before it).  The loop is built
+        // twice, with and without the bias add, and a uniform branch picks one
+        // (without a bias there is nothing to read or add).
+        auto stage_out = [&](auto with_bias) {
+            constexpr bool HB = decltype(with_bias)::value;
 #pragma unroll
-        for (int ni = 0; ni < NB; ++ni) {
-            v4f sc[4];
-            uint2 braw[4];
+            for (int ni = 0; ni < NB; ++ni) {
+                v4f sc[4];
+                uint2 braw[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lc0 = wn * WNC + ni * 32 + 8 * q + 4 * h;
-                if constexpr (!MX) sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
-                braw[q] = *reinterpret_cast<const uint2*>(lds_bias + lc0);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                for (int q = 0; q < 4; ++q) {
+                    const int lc0 = wn * WNC + ni * 32 + 8 * q + 4 * h;
+                    if constexpr (!MX) sc[q] = *reinterpret_cast<const v4f*>(lds_sb + lc0);
+                    if constexpr (HB) braw[q] = *reinterpret_cast<const uint2*>(lds_bias + lc0);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint2 b2 = braw[q];
-                const float bc[4] = {has_bias ? __uint_as_float(b2.x << 16) : -0.0f,
-                                     has_bias ? __uint_as_float(b2.x & 0xffff0000u) : -0.0f,
-                                     has_bias ? __uint_as_float(b2.y << 16) : -0.0f,
-                                     has_bias ? __uint_as_float(b2.y & 0xffff0000u) : -0.0f};
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    float v[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if constexpr (MX)
-                            v[j] = add_bias(acc[mi][ni][4 * q + j], bc[j]);
-                        else
-                            v[j] = add_bias(scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[q][j]), bc[j]);
-                        if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                for (int q = 0; q < 4; ++q) {
+                    float bc[4] = {};
+                    if constexpr (HB) {
+                        bc[0] = __uint_as_float(braw[q].x << 16);
+                        bc[1] = __uint_as_float(braw[q].x & 0xffff0000u);
+                        bc[2] = __uint_as_float(braw[q].y << 16);
+                        bc[3] = __uint_as_float(braw[q].y & 0xffff0000u);
                     }
-                    *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH + (ni * 32 + 8 * q + 4 * h) * 2) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        float v[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if constexpr (MX)
+                                v[j] = acc[mi][ni][4 * q + j];
+                            else
+                                v[j] = scale_out((float)acc[mi][ni][4 * q + j], srow[mi], sc[q][j]);
+                            if constexpr (HB) v[j] = add_bias(v[j], bc[j]);
+                            if constexpr (EPI == 1) v[j] = gelu_tanh(v[j]);
+                        }
+                        *reinterpret_cast<uint2*>(stg + (mi * 32 + fr) * EPITCH + (ni * 32 + 8 * q + 4 * h) * 2) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
                 }
             }
-        }
+        };
+        if (bias_grp != nullptr)
+            stage_out(std::true_type{});
+        else
+            stage_out(std::false_type{});
         // the wave reads back only what it wrote itself: 128 rows of 4 NB
         // 16-byte chunks (WNC columns)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
