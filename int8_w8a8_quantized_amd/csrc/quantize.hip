@@ -384,54 +384,45 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 // MXFP4 (F == 4): E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), shared
 // exponent floor(log2(amax)) - 2 (6 = 1.5 * 2^2), so the byte is
 // max(e - 2, 0); elements x * 2^-shared clamped to +-6 and rounded to the
-// nearest E2M1 value, ties to the even code.  Two codes per byte, the lower
-// index in the low nibble: a lane's 8 elements are one 32-bit store.
-__device__ __forceinline__ uint32_t e2m1_code(float t)
+// nearest E2M1 value, ties to the even code, the sign kept (-0 -> 0x8).  Two
+// codes per byte, the lower index in the low nibble: a lane's 8 elements are
+// one 32-bit store.  gfx950 converts BF16 pairs this way in one instruction,
+// v_cvt_scalef32_pk_fp4_bf16, which divides by the scale operand (the
+// power of two 2^shared): on every finite BF16 input under scales 2^-127 ..
+// 2^125 it gives the E2M1 codes of that rule (the MXFP4 quantiser tests
+// check it against the oracle on every finite BF16 value).
+typedef __bf16 v2bf_mx __attribute__((ext_vector_type(2)));
+
+// 2^(code - 127) for an E8M0 byte (2^-127, the byte 0, is a binary32 subnormal)
+__device__ __forceinline__ float e8m0_value(int code)
 {
-    // the thresholds are the midpoints of the grid; at a midpoint the even
-    // code wins (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
-    // 3.5 -> 4, 5 -> 4), and everything above 5 saturates to 6
-    const float a = __builtin_fabsf(t);
-    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(t) >> 28) & 8u);
+    return __uint_as_float(code > 0 ? (uint32_t)code << 23 : 0x00400000u);
 }
 
-__device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float inv)
+__device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float scale)
 {
-    return e2m1_code(bf_lo(w.x) * inv) | (e2m1_code(bf_hi(w.x) * inv) << 4) |
-           (e2m1_code(bf_lo(w.y) * inv) << 8) | (e2m1_code(bf_hi(w.y) * inv) << 12) |
-           (e2m1_code(bf_lo(w.z) * inv) << 16) | (e2m1_code(bf_hi(w.z) * inv) << 20) |
-           (e2m1_code(bf_lo(w.w) * inv) << 24) | (e2m1_code(bf_hi(w.w) * inv) << 28);
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(v2bf_mx, w.x), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf_mx, w.y), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf_mx, w.z), scale, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf_mx, w.w), scale, 3);
 }
 
 // MXFP6 (F == 62: E2M3, bias 1, largest 7.5; F == 63: E3M2, bias 3, largest
-// 28): shared exponent floor(log2(amax)) - emax (2 / 4).  The code of a
-// scaled element t (|t| clamped to the largest value) is
-//   2^mb (e - emin) + rint(|t| 2^(mb - e)),  e = max(floor(log2 |t|), emin),
-// with mb mantissa bits and emin = 1 - bias: rint (ties to even) of the
-// exactly scaled value picks the nearest grid point, the even code on a tie,
-// and a carry into the next binade lands on its first code.  Six-bit codes
-// are stored group-major: the 128 codes of group g of row r are a 96-byte
-// little-endian bit stream at byte (g rows + r) 96, so the groups of one K
-// range of all rows lie together (a GEMM stage reads a contiguous panel).
-template <int MB, int EMIN>
-__device__ __forceinline__ uint32_t small_float_code(float v, float vmax)
-{
-    const float t = __builtin_fminf(__builtin_fabsf(v), vmax);
-    const int e = max((int)((__float_as_uint(t) >> 23) & 0xFFu) - 127, EMIN);
-    const float up = __uint_as_float((uint32_t)(127 + MB - e) << 23);  // 2^(mb - e)
-    return (uint32_t)((e - EMIN) << MB) + (uint32_t)__builtin_rintf(t * up);
-}
-
-template <int F>
-__device__ __forceinline__ uint32_t fp6_code(float v)
-{
-    constexpr int MB = F == 62 ? 3 : 2, EMIN = F == 62 ? 0 : -2;
-    constexpr float VMAX = F == 62 ? 7.5f : 28.0f;
-    return small_float_code<MB, EMIN>(v, VMAX) | ((__float_as_uint(v) >> 26) & 32u);
-}
+// 28): shared exponent floor(log2(amax)) - emax (2 / 4); elements
+// x * 2^-shared clamped to the largest value and rounded to the nearest grid
+// point, ties to the even code, the sign kept.  Six-bit codes are stored
+// group-major: the 128 codes of group g of row r are a 96-byte
+// little-endian bit stream (four codes in three bytes) at byte
+// (g rows + r) 96, so the groups of one K range of all rows lie together (a
+// GEMM stage reads a contiguous panel).  gfx950 converts 32 BF16 values this
+// way in one instruction, v_cvt_scalef32_pk32_fp6_bf16 (E2M3) /
+// v_cvt_scalef32_pk32_bf6_bf16 (E3M2), dividing by the scale operand (the
+// power of two 2^shared) and writing the 32 codes as 24 bytes of that bit
+// stream: on every finite BF16 input under scales 2^-127 .. 2^125 it gives
+// the codes of the rule above (the MXFP6 quantiser tests check it against
+// the oracle on every finite BF16 value).
+typedef __bf16 v32bf_mx __attribute__((ext_vector_type(32)));
+typedef int v6i_mx __attribute__((ext_vector_type(6)));
 
 template <int F>  // 8: MXFP8 (E4M3FN), 4: MXFP4 (E2M1)
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ x,
@@ -481,7 +472,7 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
                                            bf_hi(w.w) * inv, 448.0f);
                     reinterpret_cast<uint2*>(qrow)[idx] = o;
                 } else {
-                    reinterpret_cast<uint32_t*>(qrow)[idx] = e2m1_pack8(w, inv);
+                    reinterpret_cast<uint32_t*>(qrow)[idx] = e2m1_pack8(w, e8m0_value(code));
                 }
                 if ((lane & 15) == 0) scale[(int64_t)(idx >> 4) * rows + row] = word;
             }
@@ -489,14 +480,36 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
     }
 }
 
-// MXFP6: 16 rows per workgroup, one 128-element group of each at a time.
-// Lane l of wave w takes row 4 w + (l >> 4) of the workgroup and chunk
-// l & 15 (8 elements) of the group, so a 16-lane DPP row is one group of one
-// row, as in quantize_mx_kernel, and the workgroup writes a group's codes
-// for its 16 rows as one contiguous 1536-byte run of the group-major array
-// (one wave per row scattered 96-byte pieces over every group's region:
-// 22% slower on a 75600 x 13824 input).  A lane's 8 codes are 6 bytes, and
-// lane pairs write their 12 bytes as one store.
+// One round of a 4 x 4 transpose across a lane quad: element u of lane q
+// takes element u ^ R of lane q ^ R where bit R of q ^ u is set.
+template <int R>
+__device__ __forceinline__ void quad_exchange(uint32_t (&a)[4][4], int qd)
+{
+    constexpr int kPerm = R == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    uint32_t b[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[u ^ R][k], kPerm, 0xF, 0xF, false);
+            b[u][k] = ((qd ^ u) & R) ? p : a[u][k];
+        }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[u][k] = b[u][k];
+}
+
+// MXFP6: 16 rows per workgroup, four 128-element groups of each at a time.
+// Lane l of wave w takes row 4 w + (l >> 4) and loads chunk c = l & 15 (8
+// elements) of each of the four groups, so a 16-lane DPP row reads a row's
+// groups as whole 256-byte pieces.  A 4 x 4 transpose inside each lane quad
+// (two DPP exchange rounds) then gives lane q of quad j the four chunks of
+// block j of group q: one 32-element block per lane, as the conversion
+// takes them.  The workgroup writes a group's codes for its 16 rows as one
+// contiguous 1536-byte run of the group-major array (one wave per row
+// scattered 96-byte pieces over every group's region: 22% slower on a
+// 75600 x 13824 input).
 template <int F>  // 62: E2M3, 63: E3M2
 __global__ __launch_bounds__(256) void quantize_mx6_kernel(const uint16_t* __restrict__ x,
                                                            int64_t rows, int64_t cols, int64_t ld,
@@ -504,49 +517,59 @@ __global__ __launch_bounds__(256) void quantize_mx6_kernel(const uint16_t* __res
                                                            uint32_t* __restrict__ scale)
 {
     constexpr int kEmax = F == 63 ? 4 : 2;
-    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int lane = threadIdx.x & 63, c = lane & 15, qd = lane & 3, blk = c >> 2;
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const bool live = row < rows;
     const uint4* xr = reinterpret_cast<const uint4*>(x + (live ? row : 0) * ld);
     const int groups = (int)(cols >> 7);
-    constexpr int U = 4;
-    for (int g0 = 0; g0 < groups; g0 += U) {
-        uint4 v[U];
+    for (int g0 = 0; g0 < groups; g0 += 4) {
+        uint32_t a[4][4];  // [group u][dword] of the lane's chunk
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = live && g0 + u < groups ? xr[(g0 + u) * 16 + c] : make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < 4; ++u) {
+            const uint4 t = live && g0 + u < groups ? xr[(g0 + u) * 16 + c] : make_uint4(0u, 0u, 0u, 0u);
+            a[u][0] = t.x, a[u][1] = t.y, a[u][2] = t.z, a[u][3] = t.w;
+        }
+        // transpose: element u of lane q <- element q of lane u, in two
+        // rounds (lanes and elements paired by xor 1, then by xor 2)
+        quad_exchange<1>(a, qd);
+        quad_exchange<2>(a, qd);
+        // the lane now holds chunks 0..3 (a[0..3]) of block blk of group g0 + qd
+        const int g = g0 + qd;
+        uint32_t m = 0u;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int g = g0 + u;
-            uint32_t m = abs_max_chunk(0u, v[u]);
-            m = max(m & 0xFFFFu, m >> 16);
-            // block max over the 4 lanes of the quad
-            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
-            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
-            const int code = max((int)((m >> 7) & 0xFFu) - kEmax, 0);
-            const float inv = __uint_as_float((uint32_t)(254 - code) << 23);  // 2^(127 - code)
-            // the codes of the group's other 3 blocks (lanes +4, +8, +12 of the
-            // 16-lane DPP row) into the group's first lane
-            const uint32_t word = (uint32_t)code |
-                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
-                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
-                                  ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
-            const uint4 w = v[u];
-            const uint32_t c0 = fp6_code<F>(bf_lo(w.x) * inv), c1 = fp6_code<F>(bf_hi(w.x) * inv),
-                           c2 = fp6_code<F>(bf_lo(w.y) * inv), c3 = fp6_code<F>(bf_hi(w.y) * inv),
-                           c4 = fp6_code<F>(bf_lo(w.z) * inv), c5 = fp6_code<F>(bf_hi(w.z) * inv),
-                           c6 = fp6_code<F>(bf_lo(w.w) * inv), c7 = fp6_code<F>(bf_hi(w.w) * inv);
-            const uint32_t lo = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18) | (c4 << 24) | (c5 << 30);
-            const uint32_t hi = (c5 >> 2) | (c6 << 4) | (c7 << 10);  // 16 bits
-            const uint32_t plo = (uint32_t)__shfl_xor((int)lo, 1);
-            const uint32_t phi = (uint32_t)__shfl_xor((int)hi, 1);
-            if (live && g < groups) {
-                uint8_t* qg = q + ((int64_t)g * rows + row) * 96;
-                if ((c & 1) == 0)
-                    *reinterpret_cast<uint3*>(qg + (c >> 1) * 12) =
-                        make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
-                if (c == 0) scale[(int64_t)g * rows + row] = word;
+        for (int i = 0; i < 4; ++i) m = abs_max_chunk(m, make_uint4(a[i][0], a[i][1], a[i][2], a[i][3]));
+        m = max(m & 0xFFFFu, m >> 16);
+        const int code = max((int)((m >> 7) & 0xFFu) - kEmax, 0);
+        // the group's scale word into its block-0 lane: blocks 0, 2, 1, 3 (lanes
+        // +0, +8, +4, +12 of the 16-lane DPP row) in bytes 0..3
+        const uint32_t word = (uint32_t)code |
+                              ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x108, 0xF, 0xF, false) << 8) |
+                              ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x104, 0xF, 0xF, false) << 16) |
+                              ((uint32_t)__builtin_amdgcn_update_dpp(0, code, 0x10C, 0xF, 0xF, false) << 24);
+        v32bf_mx e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const v2bf_mx pr = __builtin_bit_cast(v2bf_mx, a[i][k]);
+                e[8 * i + 2 * k] = pr[0];
+                e[8 * i + 2 * k + 1] = pr[1];
             }
+        v6i_mx r6;
+        if constexpr (F == 62)
+            r6 = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(e, e8m0_value(code));
+        else
+            r6 = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(e, e8m0_value(code));
+        if (live && g < groups) {
+            // 24 bytes at block offset 24 blk: an even block starts 16-byte
+            // aligned (16 + 8 bytes), an odd one 8 bytes past (8 + 16)
+            uint8_t* qb = q + ((int64_t)g * rows + row) * 96 + blk * 24;
+            const bool odd = blk & 1;
+            *reinterpret_cast<uint4*>(qb + (odd ? 8 : 0)) =
+                odd ? make_uint4(r6[2], r6[3], r6[4], r6[5]) : make_uint4(r6[0], r6[1], r6[2], r6[3]);
+            *reinterpret_cast<uint2*>(qb + (odd ? 0 : 16)) =
+                odd ? make_uint2(r6[0], r6[1]) : make_uint2(r6[4], r6[5]);
+            if (blk == 0) scale[(int64_t)g * rows + row] = word;
         }
     }
 }

@@ -93,3 +93,33 @@ def mx_ungrouped(s):
     """Library layout [cols/128, rows, 4] -> oracle scales [rows, cols/32]."""
     g, r, _ = s.shape
     return np.ascontiguousarray(s[:, :, MX_ORDER].transpose(1, 0, 2).reshape(r, 4 * g))
+
+
+def every_bf16_blocks(kemax: int, shared_list, cols: int = 4096) -> np.ndarray:
+    """BF16 rows that put every finite BF16 value through an MX quantiser
+    under each shared exponent in shared_list.  For shared exponent S the
+    block amax is the largest BF16 value of exponent field S + 127 + kemax
+    (kemax: exponent of the element type's largest normal), so the block's
+    E8M0 byte is S + 127; each 32-element block is that amax (alternating
+    sign) followed by 31 values of magnitude at most it, every such BF16
+    value of both signs once.  For S = -127 the amax is the largest value
+    with exponent field kemax (every smaller amax also gives the byte 0).
+    Rows of `cols` elements; the tail is padded with zeros."""
+    blocks = []
+    mag = np.arange(0x7F80, dtype=np.uint32)  # finite magnitudes (bits)
+    for S in shared_list:
+        e = S + 127 + kemax if S > -127 else kemax
+        assert 1 <= e <= 254, S
+        amax = np.uint32((e << 7) | 0x7F)
+        vals = mag[mag <= amax]
+        vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+        nb = (vals.size + 30) // 31
+        body = np.zeros(nb * 31, dtype=np.uint16)
+        body[:vals.size] = vals
+        head = np.where(np.arange(nb) % 2 == 0, amax, amax | 0x8000).astype(np.uint16)
+        blocks.append(np.concatenate([head[:, None], body.reshape(nb, 31)], axis=1))
+    b = np.concatenate(blocks, axis=0).reshape(-1)
+    rows = (b.size + cols - 1) // cols
+    out = np.zeros(rows * cols, dtype=np.uint16)
+    out[:b.size] = b
+    return out.reshape(rows, cols)

@@ -14,8 +14,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, mx_grouped,
-                      mx_ungrouped, needs_gpu, say)
+from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, every_bf16_blocks, host_bits,
+                      mx_grouped, mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -33,6 +33,20 @@ def _blocky(rng, rows, cols, sigma=1.0, spread=6):
     x = x * gain
     x[rng.random((rows, cols)) < 0.01] *= 16
     return synth.to_bf16_bits(x.astype(np.float32))
+
+
+def test_quantize_mxfp4_every_bf16_value(tfq):
+    """Every finite BF16 value, both signs, through the quantiser under the
+    shared exponents -127 (the E8M0 byte 0), -126, -20, -1, 0, 1, 20 and
+    125: codes and scale bytes bit for bit against the oracle (this pins the
+    hardware's scaled E2M1 conversion, saturation and ties included)."""
+    xb = every_bf16_blocks(2, [-127, -126, -20, -1, 0, 1, 20, 125])
+    say(f"mxfp4 every bf16 value rows={xb.shape[0]} cols={xb.shape[1]}")
+    q, s = tfq.tfq_quantize_mxfp4(dev_bf16(xb))
+    torch.cuda.synchronize()
+    q_e, s_e = orc.quantize_mx4(xb)
+    assert np.array_equal(mx_ungrouped(host_bits(s)), s_e)
+    assert np.array_equal(host_bits(q), q_e)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 128), (300, 1152), (7, 13824), (64, 8192 + 128)])

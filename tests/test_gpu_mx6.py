@@ -16,8 +16,8 @@ import torch
 
 import oracle as orc
 import synth
-from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, host_bits, mx6_grouped,
-                      mx6_ungrouped, mx_grouped, mx_ungrouped, needs_gpu, say)
+from gpu_util import (assert_fp8_tolerance, dev_bf16, dev_u8, every_bf16_blocks, host_bits,
+                      mx6_grouped, mx6_ungrouped, mx_grouped, mx_ungrouped, needs_gpu, say)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -58,6 +58,23 @@ def test_quantize_mxfp6_bit_exact(tfq, fmt, rows, cols):
     qe, se = orc.quantize_mx6(xb, fmt)
     assert np.array_equal(mx_ungrouped(host_bits(s)), se)
     assert np.array_equal(mx6_ungrouped(host_bits(q)), qe)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_mxfp6_every_bf16_value(tfq, fmt):
+    """Every finite BF16 value, both signs, through the quantiser under
+    shared exponents from -127 (the E8M0 byte 0) to the largest the format's
+    amax allows: codes and scale bytes bit for bit against the oracle (this
+    pins the hardware's scaled 6-bit conversion, saturation and ties
+    included)."""
+    kemax = 2 if fmt == "e2m3" else 4
+    xb = every_bf16_blocks(kemax, [-127, -126, -20, -1, 0, 1, 20, 127 - kemax])
+    say(f"mxfp6 {fmt} every bf16 value rows={xb.shape[0]} cols={xb.shape[1]}")
+    q, s = tfq.tfq_quantize_mxfp6(dev_bf16(xb), fmt)
+    torch.cuda.synchronize()
+    q_e, s_e = orc.quantize_mx6(xb, fmt)
+    assert np.array_equal(mx_ungrouped(host_bits(s)), s_e)
+    assert np.array_equal(mx6_ungrouped(host_bits(q)), q_e)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
