@@ -399,9 +399,10 @@ __global__ __launch_bounds__(256) void quantize_groups128(
 // codes per byte, the lower index in the low nibble: a lane's 8 elements are
 // one 32-bit store.  gfx950 converts BF16 pairs this way in one instruction,
 // v_cvt_scalef32_pk_fp4_bf16, which divides by the scale operand (the
-// power of two 2^shared): on every finite BF16 input under scales 2^-127 ..
-// 2^125 it gives the E2M1 codes of that rule (the MXFP4 quantiser tests
-// check it against the oracle on every finite BF16 value).
+// power of two 2^shared): on every finite BF16 input, under each scale
+// tried from 2^-127 to 2^125, it gives the E2M1 codes of that rule (the
+// MXFP4 quantiser tests check it against the oracle on every finite BF16
+// value under eight such scales).
 typedef __bf16 v2bf_mx __attribute__((ext_vector_type(2)));
 
 // 2^(code - 127) for an E8M0 byte (2^-127, the byte 0, is a binary32 subnormal)
@@ -429,9 +430,10 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const uint4& w, float scale)
 // way in one instruction, v_cvt_scalef32_pk32_fp6_bf16 (E2M3) /
 // v_cvt_scalef32_pk32_bf6_bf16 (E3M2), dividing by the scale operand (the
 // power of two 2^shared) and writing the 32 codes as 24 bytes of that bit
-// stream: on every finite BF16 input under scales 2^-127 .. 2^125 it gives
-// the codes of the rule above (the MXFP6 quantiser tests check it against
-// the oracle on every finite BF16 value).
+// stream: on every finite BF16 input, under each scale tried from 2^-127 to
+// 2^125, it gives the codes of the rule above (the MXFP6 quantiser tests
+// check it against the oracle on every finite BF16 value under eight such
+// scales).
 typedef __bf16 v32bf_mx __attribute__((ext_vector_type(32)));
 typedef int v6i_mx __attribute__((ext_vector_type(6)));
 
